@@ -1,0 +1,142 @@
+"""Masked softmax attention over explicit connectivity sets, in float64 (oracle).
+
+Test infrastructure only (see ``oracle/__init__.py`` for the citation tags and
+the list of who may import this).  The definition followed throughout is the
+unified form of [PP] §11.1 and [KB] §2 (alpha^SWA, o^SWA): for a query position
+t with connectivity set S_t,
+
+    e_s = scale * (q_t . k_s),   alpha_ts = exp(e_s) / sum_{s' in S_t} exp(e_s'),
+    o_t = sum_{s in S_t} alpha_ts v_s,
+
+with scale = 1/sqrt(d_h) by default ([KB] §2, [MB] scaled dot product).
+The softmax is the plain two-pass form (subtract the row maximum, exponentiate,
+sum); there is no streaming, tiling or reordering.  ``lse`` is the natural log
+of sum_s exp(e_s) (m + ln l), reported so split-softmax merges can be checked.
+
+Inputs are arrays of the exact values the kernels consume (bf16 values widened
+exactly to float32/float64 by the caller); everything is cast to float64 here.
+"""
+
+import math
+
+import numpy as np
+
+from .index_sets import causal_index_set, decode_index_set, longformer_index_set
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def attend(q_row, K, V, scale):
+    """One query row over the key/value rows of its connectivity set.
+
+    Returns (o [d_v], lse).  An empty set yields o = 0 and lse = -inf (a reading:
+    the pages never produce an empty window; only an empty ring cache does).
+    """
+    q_row = _f64(q_row)
+    K = _f64(K)
+    V = _f64(V)
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[-1], dtype=np.float64), -math.inf
+    e = (K @ q_row) * float(scale)            # scores over S_t
+    m = e.max()
+    p = np.exp(e - m)                        # weights before normalisation
+    l = p.sum()
+    o = (p @ V) / l
+    return o, m + math.log(l)
+
+
+def _default_scale(d_h, scale):
+    return 1.0 / math.sqrt(d_h) if scale is None else float(scale)
+
+
+def swa_prefill(q, k, v, W, scale=None, rows=None):
+    """Causal sliding-window prefill with grouped-query heads.
+
+    q: [B, T, H_q, d_h]; k, v: [B, T, H_kv, d_h]; query head h reads key/value
+    head h // (H_q / H_kv) (contiguous groups; [ST] "Combining SWA with GQA"
+    fixes only that several query heads share one key/value head, the grouping
+    is a reading).  S_t is the causal window of ``causal_index_set``.
+    ``rows`` optionally restricts the computation to those query positions.
+    Returns o [B, R, H_q, d_h] and lse [B, H_q, R] (R = len(rows) or T).
+    """
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    group = Hq // Hkv
+    sc = _default_scale(D, scale)
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, len(rows), Hq, v.shape[-1]), dtype=np.float64)
+    lse = np.zeros((B, Hq, len(rows)), dtype=np.float64)
+    for b in range(B):
+        for ri, t in enumerate(rows):
+            S = causal_index_set(int(t), W)
+            for h in range(Hq):
+                kvh = h // group
+                o[b, ri, h], lse[b, h, ri] = attend(q[b, t, h], k[b, S, kvh], v[b, S, kvh], sc)
+    return o, lse
+
+
+def swa_decode(q, k_cache, v_cache, slot_pos, cur_pos, W, scale=None):
+    """One new query token per request over a ring cache of W slots.
+
+    q: [B, H_q, d_h]; k_cache, v_cache: [B, H_kv, W, d_h]; slot_pos: [B, W]
+    absolute position held by each slot (< 0 = empty); cur_pos: [B].
+    Attended slots are those of ``decode_index_set`` ([KB] §2 "KV cache",
+    [G3] "How it works").  Returns o [B, H_q, d_h], lse [B, H_q].
+    """
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    group = Hq // Hkv
+    sc = _default_scale(D, scale)
+    o = np.zeros((B, Hq, v_cache.shape[-1]), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    for b in range(B):
+        S = decode_index_set(slot_pos[b], int(cur_pos[b]), W)
+        for h in range(Hq):
+            kvh = h // group
+            o[b, h], lse[b, h] = attend(q[b, h], k_cache[b, kvh, S], v_cache[b, kvh, S], sc)
+    return o, lse
+
+
+def swa_longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, rows=None, heads=None):
+    """Longformer-style bidirectional attention: per-head dilated window + globals.
+
+    q, k, v: [B, T, H, d_h]; dilation: [H] ints >= 1 (None = all 1);
+    global_idx: [B, G] positions (None or G = 0 = no globals).
+    S_i follows ``longformer_index_set`` ([PP] §1.1, §3.1, §4.3).
+    ``rows``/``heads`` optionally restrict the computation.
+    Returns o [B, R, H', d_h], lse [B, H', R].
+    """
+    B, T, H, D = q.shape
+    sc = _default_scale(D, scale)
+    dil = [1] * H if dilation is None else [int(x) for x in dilation]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = list(range(H)) if heads is None else list(heads)
+    o = np.zeros((B, len(rows), len(heads), v.shape[-1]), dtype=np.float64)
+    lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
+    for b in range(B):
+        G = () if global_idx is None else [int(g) for g in np.asarray(global_idx)[b]]
+        for hi, h in enumerate(heads):
+            for ri, i in enumerate(rows):
+                S = longformer_index_set(int(i), T, r, dil[h], G)
+                o[b, ri, hi], lse[b, hi, ri] = attend(q[b, i, h], k[b, S, h], v[b, S, h], sc)
+    return o, lse
+
+
+def dense_masked_attention(q, k, v, mask, scale):
+    """The literal dense form of [KB] §3 (and [MB]'s four steps): full [T, T]
+    scores, masked_fill(~mask, -inf), row softmax, then weights @ V.
+
+    q, k: [T, d]; v: [T, d_v]; mask: bool [T, T].  Used only to cross-check the
+    index-set form on small inputs.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    scores = (q @ k.T) * float(scale)
+    scores = np.where(mask, scores, -np.inf)
+    mx = scores.max(axis=1, keepdims=True)
+    p = np.exp(scores - mx)
+    attn = p / p.sum(axis=1, keepdims=True)
+    return attn @ v

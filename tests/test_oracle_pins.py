@@ -1,0 +1,329 @@
+"""Pins for the CPU oracle: printed tables, closed forms, textbook special cases
+and brute force.  None of these recomputes the oracle's own formula; each pits
+the oracle against something fixed independently of it.  CPU only.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import logsumexp
+
+import oracle
+from oracle import index_sets as ix
+from sliding_window_attention_amd import inputs as inp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_table(name):
+    rows, total = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, vals = line.split(":")
+            if key == "total":
+                total = int(vals)
+            else:
+                rows[int(key)] = [int(x) for x in vals.split()]
+    return rows, total
+
+
+# ---------------------------------------------------------------- printed tables
+
+def test_symmetric_table_n16_r2():
+    rows, total = _read_table("pp_symmetric_n16_r2.txt")
+    for i, keys in rows.items():
+        assert oracle.symmetric_index_set(i, 16, 2).tolist() == keys
+    sizes = [len(oracle.symmetric_index_set(i, 16, 2)) for i in range(16)]
+    assert sizes == [3, 4] + [5] * 12 + [4, 3]
+    assert sum(sizes) == total == 74
+
+
+def test_dilated_table_n16_r2_d2():
+    rows, total = _read_table("pp_dilated_n16_r2_d2.txt")
+    assert len(rows) == 16
+    for i, keys in rows.items():
+        assert oracle.longformer_index_set(i, 16, 2, 2).tolist() == keys
+    assert sum(len(oracle.longformer_index_set(i, 16, 2, 2)) for i in range(16)) == total == 68
+
+
+def test_global_table_n16_r2():
+    rows, total = _read_table("pp_global_n16_r2_G0_8.txt")
+    assert len(rows) == 16
+    for i, keys in rows.items():
+        assert oracle.longformer_index_set(i, 16, 2, 1, (0, 8)).tolist() == keys
+    assert sum(len(oracle.longformer_index_set(i, 16, 2, 1, (0, 8))) for i in range(16)) == total == 120
+    # the page's upper bound g*n + (n-g)(2r+1+g) holds
+    assert total <= 2 * 16 + 14 * (5 + 2)
+
+
+def test_counts_n16():
+    with open(os.path.join(GOLDEN, "pp_counts_n16.txt")) as f:
+        want = dict(l.split() for l in f if l.strip() and not l.startswith("#"))
+    full = sum(len(oracle.symmetric_index_set(i, 16, 15)) for i in range(16))
+    causal = sum(len(oracle.causal_index_set(t, 16)) for t in range(16))
+    window = sum(len(oracle.symmetric_index_set(i, 16, 2)) for i in range(16))
+    assert full == int(want["full_bidirectional"])
+    assert causal == int(want["full_causal"])
+    assert window == int(want["sliding_window_r2"])
+
+
+def test_causal_examples():
+    with open(os.path.join(GOLDEN, "causal_examples.txt")) as f:
+        cases = [tuple(map(int, l.split())) for l in f if l.strip() and not l.startswith("#")]
+    assert len(cases) == 3
+    for t, W, first, last in cases:
+        S = oracle.causal_index_set(t, W)
+        assert S[0] == first and S[-1] == last and len(S) == last - first + 1
+
+
+# ---------------------------------------------------------------- closed forms (brute force)
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 33])
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 16, 40])
+def test_causal_count_closed_form(T, W):
+    got = sum(len(oracle.causal_index_set(t, W)) for t in range(T))
+    w = min(W, T)
+    assert got == T * w - w * (w - 1) // 2
+
+
+@pytest.mark.parametrize("n", [8, 16, 31])
+@pytest.mark.parametrize("r", [0, 1, 2, 3])
+@pytest.mark.parametrize("d", [1, 2, 3])
+def test_dilated_count_closed_form(n, r, d):
+    if r * d > n:
+        pytest.skip("closed form assumes r*d <= n")
+    got = sum(len(oracle.symmetric_index_set(i, n, r, d)) for i in range(n))
+    assert got == (2 * r + 1) * n - d * r * (r + 1)
+
+
+def test_dilated_is_residue_class_problem():
+    # A dilated window on x equals d independent undilated windows on x[rho::d].
+    n, r, d = 23, 3, 3
+    for i in range(n):
+        rho, ii = i % d, i // d
+        m = len(range(rho, n, d))
+        want = [rho + d * j for j in oracle.symmetric_index_set(ii, m, r, 1)]
+        assert oracle.symmetric_index_set(i, n, r, d).tolist() == want
+
+
+def test_masks_match_index_sets():
+    T, W = 37, 9
+    m = oracle.causal_mask(T, W)
+    for t in range(T):
+        assert np.nonzero(m[t])[0].tolist() == oracle.causal_index_set(t, W).tolist()
+    lm = oracle.longformer_mask(20, 3, 2, (1, 12))
+    for i in range(20):
+        assert np.nonzero(lm[i])[0].tolist() == oracle.longformer_index_set(i, 20, 3, 2, (1, 12)).tolist()
+
+
+# ---------------------------------------------------------------- values: textbook special cases
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, causal, scale=None, mask=None):
+    # q [B,T,H,D] -> torch [B,H,T,D], float64 on CPU; GQA via enable_gqa.
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (q, k, v))
+    gqa = tq.shape[1] != tk.shape[1]
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, is_causal=causal,
+                                         scale=scale, enable_gqa=gqa)
+    return out.numpy().transpose(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (4, 2), (4, 1), (6, 3)])
+def test_window_covering_sequence_is_dense_causal(Hq, Hkv):
+    B, T, D = 2, 19, 8
+    q, k, v = _rand((B, T, Hq, D), 1), _rand((B, T, Hkv, D), 2), _rand((B, T, Hkv, D), 3)
+    want = _sdpa(q, k, v, causal=True)
+    for W in (T, T + 5, 4 * T):
+        o, _ = oracle.swa_prefill(q, k, v, W)
+        np.testing.assert_allclose(o, want, rtol=0, atol=1e-12)
+
+
+def test_explicit_scale_matches_library():
+    B, T, H, D = 1, 11, 2, 16
+    q, k, v = _rand((B, T, H, D), 4), _rand((B, T, H, D), 5), _rand((B, T, H, D), 6)
+    o, _ = oracle.swa_prefill(q, k, v, T, scale=0.37)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, True, scale=0.37), rtol=0, atol=1e-12)
+
+
+def test_symmetric_full_radius_is_dense_bidirectional():
+    B, T, H, D = 2, 13, 3, 8
+    q, k, v = _rand((B, T, H, D), 7), _rand((B, T, H, D), 8), _rand((B, T, H, D), 9)
+    o, _ = oracle.swa_longformer(q, k, v, r=T - 1)
+    np.testing.assert_allclose(o, _sdpa(q, k, v, causal=False), rtol=0, atol=1e-12)
+
+
+def test_banded_values_match_library_with_boolean_mask():
+    # The library applies a boolean mask built from the pages' printed tables
+    # (global + window, n=16): values of the oracle must agree.
+    rows, _ = _read_table("pp_global_n16_r2_G0_8.txt")
+    mask = torch.zeros(16, 16, dtype=torch.bool)
+    for i, keys in rows.items():
+        mask[i, keys] = True
+    B, T, H, D = 1, 16, 2, 64
+    q, k, v = _rand((B, T, H, D), 10), _rand((B, T, H, D), 11), _rand((B, T, H, D), 12)
+    o, _ = oracle.swa_longformer(q, k, v, r=2, global_idx=[[0, 8]])
+    np.testing.assert_allclose(o, _sdpa(q, k, v, False, mask=mask), rtol=0, atol=1e-12)
+
+
+def test_window_one_returns_own_value():
+    B, T, H, D = 1, 10, 2, 4
+    q, k, v = _rand((B, T, H, D), 13), _rand((B, T, H, D), 14), _rand((B, T, H, D), 15)
+    o, lse = oracle.swa_prefill(q, k, v, 1)
+    np.testing.assert_array_equal(o, v)
+    want_lse = np.einsum("bthd,bthd->bht", q, k) / math.sqrt(D)
+    np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-12)
+
+
+def test_zero_query_gives_window_mean():
+    B, T, H, D, W = 1, 25, 1, 3, 6
+    q = np.zeros((B, T, H, D))
+    k, v = _rand((B, T, H, D), 16), _rand((B, T, H, D), 17)
+    o, lse = oracle.swa_prefill(q, k, v, W)
+    csum = np.concatenate([np.zeros((1, D)), np.cumsum(v[0, :, 0], axis=0)])
+    for t in range(T):
+        lo = max(0, t - W + 1)
+        np.testing.assert_allclose(o[0, t, 0], (csum[t + 1] - csum[lo]) / (t + 1 - lo), atol=1e-12)
+        assert abs(lse[0, 0, t] - math.log(t + 1 - lo)) < 1e-12
+
+
+def test_constant_values_pass_through():
+    B, T, H, D = 1, 17, 2, 5
+    q, k = _rand((B, T, H, D), 18), _rand((B, T, H, D), 19)
+    v = np.full((B, T, H, D), 2.5)
+    o, _ = oracle.swa_prefill(q, k, v, 4)
+    np.testing.assert_allclose(o, v, atol=1e-13)
+    o, _ = oracle.swa_longformer(q, k, v, 2, [3, 2], [[0, 9]])
+    np.testing.assert_allclose(o, v, atol=1e-13)
+
+
+def test_dense_form_equals_index_set_form():
+    T, D, W = 31, 6, 7
+    q, k, v = _rand((T, D), 20), _rand((T, D), 21), _rand((T, D), 22)
+    sc = 0.3
+    dense = oracle.dense_masked_attention(q, k, v, oracle.causal_mask(T, W), sc)
+    o, _ = oracle.swa_prefill(q[None, :, None], k[None, :, None], v[None, :, None], W, sc)
+    np.testing.assert_allclose(o[0, :, 0], dense, atol=1e-13)
+    mask = oracle.longformer_mask(T, 3, 2, (5, 20))
+    dense = oracle.dense_masked_attention(q, k, v, mask, sc)
+    o, _ = oracle.swa_longformer(q[None, :, None], k[None, :, None], v[None, :, None], 3, [2], [[5, 20]], sc)
+    np.testing.assert_allclose(o[0, :, 0], dense, atol=1e-13)
+
+
+def test_lse_is_logsumexp_and_merges():
+    rng = np.random.default_rng(23)
+    D, n = 8, 50
+    q, K, V = rng.standard_normal(D), rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    sc = 0.5
+    o, lse = oracle.attend(q, K, V, sc)
+    assert abs(lse - logsumexp(K @ q * sc)) < 1e-12
+    # splitting the key set and merging the two partial results by their lse
+    # reproduces the whole (softmax associativity, used by split-KV kernels)
+    cut = 17
+    o1, l1 = oracle.attend(q, K[:cut], V[:cut], sc)
+    o2, l2 = oracle.attend(q, K[cut:], V[cut:], sc)
+    L = np.logaddexp(l1, l2)
+    np.testing.assert_allclose(np.exp(l1 - L) * o1 + np.exp(l2 - L) * o2, o, atol=1e-13)
+    assert abs(L - lse) < 1e-12
+
+
+def test_empty_set():
+    o, lse = oracle.attend(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)), 1.0)
+    assert np.all(o == 0) and lse == -math.inf
+
+
+# ---------------------------------------------------------------- ring cache / decode
+
+def test_ring_slot_rule_and_generator_state():
+    B, T, H, D, W = 3, 40, 2, 4, 8
+    k, v = _rand((B, T, H, D), 24), _rand((B, T, H, D), 25)
+    upto = np.array([3, 17, 39])
+    kc, vc, sp = oracle.ring_from_sequence(k, v, upto, W)
+    for b in range(B):
+        for j in range(W):
+            p = sp[b, j]
+            if p >= 0:
+                assert p % W == j and p <= upto[b] and p > upto[b] - W
+                np.testing.assert_array_equal(kc[b, :, j], k[b, p])
+    # the input generator's closed-form ring state is the replayed state
+    np.testing.assert_array_equal(inp.full_ring_positions(upto, W), sp)
+
+
+def test_ring_write_overwrites_position_minus_W():
+    W = 4
+    kc = np.zeros((1, 1, W, 2)); vc = np.zeros((1, 1, W, 2)); sp = np.full((1, W), -1)
+    for p in range(9):
+        oracle.ring_write(kc, vc, sp, np.full((1, 1, 2), p), np.full((1, 1, 2), -p), [p])
+    assert sorted(sp[0].tolist()) == [5, 6, 7, 8]
+    assert kc[0, 0, 8 % W, 0] == 8
+
+
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_decode_equals_prefill_row(W):
+    B, T, Hq, Hkv, D = 3, 30, 4, 2, 8
+    q, k, v = _rand((B, T, Hq, D), 26), _rand((B, T, Hkv, D), 27), _rand((B, T, Hkv, D), 28)
+    cur = np.array([0, 5, 29])
+    kc, vc, sp = oracle.ring_from_sequence(k, v, cur, W)
+    qd = np.stack([q[b, cur[b]] for b in range(B)])
+    o, lse = oracle.swa_decode(qd, kc, vc, sp, cur, W)
+    for b in range(B):
+        op, lp = oracle.swa_prefill(q[b:b + 1], k[b:b + 1], v[b:b + 1], W, rows=[cur[b]])
+        np.testing.assert_allclose(o[b], op[0, 0], atol=1e-13)
+        np.testing.assert_allclose(lse[b], lp[0, :, 0], atol=1e-12)
+
+
+def test_decode_ignores_slot_order_and_masks_stale_future_empty():
+    rng = np.random.default_rng(29)
+    B, Hq, Hkv, D, W = 1, 2, 1, 4, 6
+    q = rng.standard_normal((B, Hq, D))
+    kc, vc = rng.standard_normal((B, Hkv, W, D)), rng.standard_normal((B, Hkv, W, D))
+    sp = np.array([[10, 11, 12, 4, 20, -1]])      # 4 stale, 20 future, -1 empty
+    cur = np.array([12])
+    o, _ = oracle.swa_decode(q, kc, vc, sp, cur, W)
+    assert oracle.decode_index_set(sp[0], 12, W).tolist() == [0, 1, 2]
+    perm = rng.permutation(W)
+    o2, _ = oracle.swa_decode(q, kc[:, :, perm], vc[:, :, perm], sp[:, perm], cur, W)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+    # all slots invalid -> zero output
+    o3, l3 = oracle.swa_decode(q, kc, vc, np.full((1, W), -1), cur, W)
+    assert np.all(o3 == 0) and np.all(np.isneginf(l3))
+
+
+# ---------------------------------------------------------------- tiles
+
+def test_tiles_hand_example():
+    # T=16, W=4, BM=BN=4 (causal): block 0 sees only the diagonal block; later
+    # blocks see their diagonal block and the one before, both partly masked.
+    got = oracle.band_tiles_bruteforce("causal", 16, 4, 4, 4)
+    assert got[0] == ([0], [0])
+    for qi in range(1, 4):
+        assert got[qi] == ([qi - 1, qi], [qi - 1, qi])
+
+
+@pytest.mark.parametrize("W,B_", [(8, 4), (12, 4), (16, 8)])
+def test_tiles_causal_steady_state(W, B_):
+    T = 64
+    got = oracle.band_tiles_bruteforce("causal", T, W, B_, B_)
+    for qi, (vis, edge) in enumerate(got):
+        m0 = qi * B_
+        if m0 + B_ <= W:               # ramp: only the diagonal block is partial
+            assert vis == list(range(0, qi + 1)) and edge == [qi]
+        else:                          # steady state: W/BN + 1 blocks, two partial
+            assert len(vis) == W // B_ + 1 and len(edge) == 2
+            assert edge == [vis[0], vis[-1]]
+
+
+def test_tiles_ragged_tail_is_edge():
+    got = oracle.band_tiles_bruteforce("causal", 10, 100, 4, 4)
+    # last key block covers columns 8..11; 10, 11 are out of range -> partial
+    assert got[2] == ([0, 1, 2], [2])
+    assert got[1] == ([0, 1], [1])
