@@ -1,0 +1,150 @@
+/*
+ * swa.h — C ABI of libswa.so: sliding-window attention (SWA) forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For a query position t with connectivity set S_t,
+ *     o_t = sum_{s in S_t} softmax_s(scale * q_t . k_s) v_s
+ * (the masked softmax of the "Sliding Window Attention" knowledge-base page
+ * (lizeman.github.io/llm-arch-kb), §2 "Derivation", and the common form in §11.1
+ * of "Sliding Window Attention: From Local Windows to Global Context"
+ * (prathamp.com)).  The entry points differ only in S_t:
+ *   swa_prefill     causal window  t-W < s <= t                (knowledge base §2, §3)
+ *   swa_decode      ring cache of W slots, window from stored absolute positions
+ *                   (knowledge base §2 "KV cache"; "Sliding Window Attention —
+ *                   Gemma 3" study note, "How it works")
+ *   swa_longformer  symmetric window |i-j| <= r with per-head dilation and
+ *                   global tokens (prathamp.com §1.1, §3.1, §4.3)
+ *
+ * Conventions shared by every entry point.
+ *   - Tensors are caller-owned, contiguous, row-major DEVICE buffers unless an
+ *     argument says HOST.  Element type: bf16 (SWA_BF16) or float32 (SWA_F32)
+ *     for q/k/v/o; lse is always float32; positions are int32.  Device
+ *     pointers must be 16-byte aligned.
+ *   - d_h must be 64 or 128 (others: SWA_ERR_UNSUPPORTED).
+ *   - scale is the logit multiplier (1/sqrt(d_h) for the pages' attention);
+ *     it must be finite and > 0.
+ *   - Grouped-query heads: query head h reads key/value head h / (H_q / H_kv)
+ *     (contiguous groups; H_q must be a multiple of H_kv).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *     Every argument is validated on the host before any HIP call; on error
+ *     nothing is launched.  The library keeps no pointer after returning,
+ *     allocates no device memory, and has no mutable global state: concurrent
+ *     calls from several host threads are safe.
+ *   - Errors: SWA_ERR_INVALID (bad argument), SWA_ERR_UNSUPPORTED (valid but
+ *     not implemented), SWA_ERR_WORKSPACE (workspace too small), SWA_ERR_HIP
+ *     (a HIP launch failed; device faults surface at stream synchronisation).
+ *     The ABI never throws.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SWA_OK = 0,
+  SWA_ERR_INVALID = 1,
+  SWA_ERR_UNSUPPORTED = 2,
+  SWA_ERR_WORKSPACE = 3,
+  SWA_ERR_HIP = 4
+} swa_status;
+
+typedef enum { SWA_BF16 = 0, SWA_F32 = 1 } swa_dtype;
+
+/* Window families for the introspection calls. */
+enum { SWA_MODE_CAUSAL = 0, SWA_MODE_SYMMETRIC = 1 };
+
+/* Causal sliding-window prefill.
+ * Query t attends keys s with t-W < s <= t: W keys including itself, fewer at
+ * the start (knowledge base §2: N_t = [max(0, t-W+1), t]; §3 mask; the Gemma 3
+ * note's t=2000, W=1024 -> 977..2000).  W >= T is ordinary causal attention.
+ *   q, o : [B, T, H_q, d_h]          k, v : [B, T, H_kv, d_h]
+ *   lse  : [B, H_q, T] float32 natural-log sum of exp(logits), or NULL.
+ * Errors: INVALID for null q/k/v/o, B,T,H_q,H_kv < 1, W < 1, H_q % H_kv != 0,
+ * bad scale; UNSUPPORTED for other d_h. */
+swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                       float scale, void *stream);
+
+/* Decode over a rolling-buffer KV cache: one new query token per request.
+ * Token p is stored in slot p mod W (knowledge base §2 "KV cache"); every slot
+ * records the absolute position it holds, and the window is computed from those
+ * positions, not from slot offsets (Gemma 3 note, "How it works").  The caller
+ * writes the current token into its slot first (swa_cache_write) and then calls
+ * swa_decode.  Slot j is attended iff slot_pos[b][j] >= 0 and
+ * cur_pos[b]-W < slot_pos[b][j] <= cur_pos[b]; slots holding stale or future
+ * positions and empty slots (negative) are ignored.  A request with no valid
+ * slot gets o = 0 and lse = -inf.
+ *   q, o             : [B, H_q, d_h]
+ *   k_cache, v_cache : [B, H_kv, W, d_h]
+ *   slot_pos         : [B, W] int32        cur_pos : [B] int32   (device)
+ *   lse              : [B, H_q] float32 or NULL
+ *   workspace        : device scratch of at least swa_decode_workspace_size()
+ *                      bytes, 256-byte aligned, owned by the caller; contents
+ *                      need not be initialised and are overwritten.
+ * Errors: as swa_prefill, plus WORKSPACE when workspace_bytes is too small. */
+size_t swa_decode_workspace_size(int B, int H_q, int H_kv, int W, int d_h);
+swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *slot_pos, const int32_t *cur_pos, void *o, float *lse,
+                      int B, int W, int H_q, int H_kv, int d_h, float scale, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Ring-cache append: writes k_new[b], v_new[b] ([B, H_kv, d_h]) into slot
+ * pos[b] mod W of k_cache/v_cache ([B, H_kv, W, d_h]) and sets
+ * slot_pos[b][slot] = pos[b] (knowledge base §2 "KV cache": writing token p
+ * overwrites token p-W).  pos (device int32 [B]) must be >= 0. */
+swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new,
+                           const int32_t *pos, void *k_cache, void *v_cache, int32_t *slot_pos,
+                           int B, int W, int H_kv, int d_h, void *stream);
+
+/* Longformer-style bidirectional attention.
+ * A non-global row i of head h attends {i + k*dil[h] : -r <= k <= r} inside
+ * [0, T) (prathamp.com §1.1 window, §3.1 dilation, §3.6 per-head dilation mix)
+ * united with the global positions G_b, each counted once; a global row
+ * (i in G_b) attends every position 0..T-1 (prathamp.com §4.3).
+ *   q, k, v, o : [B, T, H, d_h]        lse : [B, H, T] float32 or NULL
+ *   dilation   : HOST int32 [H], each in [1, 65535], or NULL (= all 1), H <= 256
+ *   global_idx : HOST int32 [B, G]; each row strictly increasing in [0, T);
+ *                NULL iff G == 0; B*G <= 512
+ *   workspace  : device scratch of at least swa_longformer_workspace_size()
+ *                bytes (0 when G == 0), 256-byte aligned, caller-owned.
+ * Errors: INVALID for r < 0, bad dilation or global list, and the swa_prefill
+ * cases; UNSUPPORTED for other d_h, H > 256 or B*G > 512; WORKSPACE. */
+size_t swa_longformer_workspace_size(int B, int T, int H, int d_h, int G);
+swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                          float *lse, int B, int T, int H, int d_h, int r,
+                          const int32_t *dilation, const int32_t *global_idx, int G,
+                          float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- introspection (tests) ------------------------------------------------ */
+
+/* Query/key tile sizes (rows per workgroup, keys per tile) the bf16 kernels use
+ * for this entry point ('p' prefill, 'l' longformer) and head shape. */
+swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *BN);
+
+/* The band-tile schedule the kernels run (the same inline code): for each query
+ * tile qi of BM rows and each key tile kj of BN columns it visits, one triple
+ * (qi, kj, needs_mask) is written to out[3*n..3*n+2].  mode SWA_MODE_CAUSAL uses
+ * window W = w_or_r; SWA_MODE_SYMMETRIC uses radius r = w_or_r (undilated: a
+ * dilated head runs this schedule in each residue class, of length
+ * ceil((T - rho) / dil)).  Returns the number of triples (which may exceed cap;
+ * only the first cap are written), or -1 on invalid arguments.  Host only. */
+int swa_band_tiles(int mode, int T, int w_or_r, int BM, int BN, int32_t *out, int cap);
+
+/* Writes the device-side window predicate the kernels use as a uint8 [T, T]
+ * matrix (1 = attended) into mask_dev (device).  Causal: W = w_or_r.
+ * Symmetric: r = w_or_r, dilation dil, HOST global list global_idx[G]. */
+swa_status swa_debug_index_mask(int mode, int T, int w_or_r, int dil, const int32_t *global_idx,
+                                int G, uint8_t *mask_dev, void *stream);
+
+const char *swa_status_str(swa_status s);
+int swa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWA_H */

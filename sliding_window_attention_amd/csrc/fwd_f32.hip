@@ -1,0 +1,136 @@
+// fwd_f32.hip — float32 forward pass for all window families (VALU, not MFMA).
+//
+// The float32 I/O path is for callers that need full single precision; it is
+// not the performance path.  One wave computes one query row: lanes score 64
+// keys of the row's connectivity set at a time (one key per lane), keep an
+// online softmax (running max, rescaled sum), and accumulate p*v with each lane
+// owning D/64 output columns.
+//
+// Connectivity sets: causal t-W < s <= t ([KB] §2-§3); Longformer: a global
+// row attends every position, any other row attends i + k*dil (|k| <= r) inside
+// [0, T) plus the global positions not already in that window ([PP] §1.1,
+// §3.1, §4.3).  Scores use the masked softmax of [KB] §2.
+//
+// Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
+// [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com).
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+template <int D, bool SYM>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const GlobalList gl) {
+  constexpr int DPL = D / 64;  // output columns per lane
+  __shared__ float qs[4][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row_id = (long long)blockIdx.x * 4 + wave;  // (b, h, t) flattened
+  const long long n_rows = (long long)a.B * a.Hq * a.T;
+  const bool live = row_id < n_rows;
+  const int t = live ? (int)(row_id % a.T) : 0;
+  const int h = live ? (int)((row_id / a.T) % a.Hq) : 0;
+  const int b = live ? (int)(row_id / ((long long)a.T * a.Hq)) : 0;
+  const int kvh = SYM ? h : h / a.group;
+  const float *q = static_cast<const float *>(a.q);
+  const float *k = static_cast<const float *>(a.k) + (long long)b * a.k_sb + (long long)kvh * D;
+  const float *v = static_cast<const float *>(a.v) + (long long)b * a.k_sb + (long long)kvh * D;
+  for (int d = lane; d < D; d += 64)
+    qs[wave][d] = live ? q[(long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D + d] : 0.f;
+  __syncthreads();
+  if (!live) return;
+
+  // Enumerate the connectivity set as idx -> key position (or -1 = skip).
+  int n_keys, base = 0, kstep = 1, n_win = 0;
+  bool is_glob = false;
+  const int dil = SYM ? a.dil[h] : 1;
+  if constexpr (!SYM) {
+    base = max(0, t - a.W + 1);
+    n_keys = t - base + 1;
+  } else {
+    for (int g = 0; g < a.G; ++g) is_glob |= gl.idx[b * a.G + g] == t;
+    if (is_glob) {
+      n_keys = a.T;
+    } else {
+      const int r = a.W;
+      const int k_lo = max(-r, -(t / dil));
+      const int k_hi = min(r, (a.T - 1 - t) / dil);
+      base = t + k_lo * dil;
+      kstep = dil;
+      n_win = k_hi - k_lo + 1;
+      n_keys = n_win + a.G;
+    }
+  }
+
+  float m = -INFINITY, l = 0.f, acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < n_keys; c0 += 64) {
+    const int idx = c0 + lane;
+    int key = -1;
+    if (idx < n_keys) {
+      if (!SYM || is_glob) key = base + idx * kstep;
+      else if (idx < n_win) key = base + idx * kstep;
+      else {
+        const int g = gl.idx[b * a.G + idx - n_win];
+        key = dilated_in(t, g, a.W, dil) ? -1 : g;  // already counted in the window
+      }
+    }
+    float s = -INFINITY;
+    if (key >= 0) {
+      const float *kr = k + (long long)key * a.k_st;
+      float dot = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) dot = fmaf(qs[wave][d], kr[d], dot);
+      s = dot * a.sl2;  // log2 domain
+    }
+    float cm = s;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) cm = fmaxf(cm, __shfl_xor(cm, x));
+    const float m_new = fmaxf(m, cm);
+    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m - mu);
+    const float p = exp2f(s - mu);
+    float ps = p;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) ps += __shfl_xor(ps, x);
+    l = l * alpha + ps;
+    m = m_new;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] *= alpha;
+    const int cnt = min(64, n_keys - c0);
+    for (int u = 0; u < cnt; ++u) {
+      const float pu = __shfl(p, u);
+      const int ku = __shfl(key, u);
+      if (ku >= 0) {
+        const float *vr = v + (long long)ku * a.k_st;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pu, vr[lane + 64 * i], acc[i]);
+      }
+    }
+  }
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  float *o = static_cast<float *>(a.o) + (long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[lane + 64 * i] = acc[i] * inv;
+  if (a.lse && lane == 0)
+    a.lse[((long long)b * a.Hq + h) * a.T + t] = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+                          hipStream_t st) {
+  const long long rows = (long long)a.B * a.Hq * a.T;
+  const int blocks = (int)((rows + 3) / 4);
+  if (blocks <= 0) return hipSuccess;
+  if (!symmetric) {
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, false>), dim3(blocks), dim3(256), 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, false>), dim3(blocks), dim3(256), 0, st, a, *gl);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, true>), dim3(blocks), dim3(256), 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, true>), dim3(blocks), dim3(256), 0, st, a, *gl);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swa

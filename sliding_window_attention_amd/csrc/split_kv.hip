@@ -1,0 +1,305 @@
+// split_kv.hip — few queries against many keys: ring-cache decode and the
+// global rows of Longformer attention.
+//
+// Both are HBM-bound streams over keys.  The keys of one (batch, key/value
+// head) are cut into S chunks; one workgroup per chunk computes, for every
+// query sharing that head, the partial softmax state (max m, sum l and the
+// unnormalised sum of p*v) and writes it to the workspace.  A second kernel
+// merges the S partials: with M = max_s m_s, o = sum_s 2^(m_s-M) acc_s /
+// sum_s 2^(m_s-M) l_s, which equals the softmax over the union of the chunks
+// exactly up to rounding (softmax over a disjoint union).
+//
+// Decode mask: slot j is attended iff its stored absolute position p satisfies
+// p >= 0 and cur-W < p <= cur ([KB] §2 "KV cache": token p lives in slot p mod W;
+// [G3] "How it works": the window comes from stored positions).
+// Global rows: a global position attends every position ([PP] §4.3).
+//
+// Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
+// [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive);
+// [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com).
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr int kMaxQ = 8;        // queries per launch of the split kernel
+constexpr int kMaxChunk = 512;  // keys per workgroup
+
+struct alignas(16) U4 {
+  uint32_t w[4];
+};
+
+__device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// 8 consecutive elements starting at p, widened to fp32
+template <bool F32>
+__device__ inline void load8(const void *p, float *out) {
+  if constexpr (F32) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+    const U4 u = *reinterpret_cast<const U4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf_lo(u.w[i]);
+      out[2 * i + 1] = bf_hi(u.w[i]);
+    }
+  }
+}
+
+template <int D, bool F32, bool DECODE>
+__global__ __launch_bounds__(256) void split_kernel(const SplitArgs a, const GlobalList gl, int q_off,
+                                                    int nq, int G) {
+  constexpr int LPR = D / 8;          // lanes per key row
+  constexpr int RPR = 256 / LPR;      // rows per round (whole workgroup)
+  constexpr int ES = F32 ? 4 : 2;     // element size
+  __shared__ float qs[kMaxQ][D];
+  __shared__ float sc[kMaxQ][kMaxChunk];
+  __shared__ float red[4][kMaxQ][D];
+  __shared__ float ml[kMaxQ][2];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = split * a.chunk;
+  const int c1 = min(a.n_keys, c0 + a.chunk);
+  const int n = c1 - c0;
+
+  // ---- queries -> LDS (fp32)
+  for (int i = tid; i < nq * D; i += 256) {
+    const int qi = i / D, d = i % D;
+    long long off;
+    if constexpr (DECODE) off = b * a.q_sb + kvh * a.q_sh + (long long)(q_off + qi) * a.q_sq + d;
+    else off = b * a.q_sb + kvh * a.q_sh + (long long)gl.idx[b * G + q_off + qi] * a.q_sq + d;
+    float x;
+    if constexpr (F32) x = static_cast<const float *>(a.q)[off];
+    else x = __uint_as_float((uint32_t) static_cast<const uint16_t *>(a.q)[off] << 16);
+    qs[qi][d] = x;
+  }
+  __syncthreads();
+
+  const char *kb = static_cast<const char *>(a.k) + (b * a.k_sb + kvh * a.k_sh) * ES;
+  const char *vb = static_cast<const char *>(a.v) + (b * a.k_sb + kvh * a.k_sh) * ES;
+  const int grp = tid / LPR, sub = tid % LPR;  // row group, 8-column chunk
+  int cur = 0;
+  if constexpr (DECODE) cur = a.cur_pos[b];
+
+  // ---- phase 1: scores (x scale*log2 e); masked keys get -inf
+  for (int r0 = 0; r0 < n; r0 += RPR) {
+    const int r = r0 + grp;
+    float kx[8];
+    bool valid = r < n;
+    if (valid) load8<F32>(kb + ((c0 + r) * a.k_sr + sub * 8) * ES, kx);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kx[e] = 0.f;
+    if constexpr (DECODE) {
+      if (valid) {
+        const int p = a.slot_pos[(long long)b * a.n_keys + c0 + r];
+        valid = p >= 0 && p > cur - a.W && p <= cur;
+      }
+    }
+    for (int qi = 0; qi < nq; ++qi) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf(qs[qi][sub * 8 + e], kx[e], part);
+#pragma unroll
+      for (int x = 1; x < LPR; x <<= 1) part += __shfl_xor(part, x);
+      if (sub == 0 && r < n) sc[qi][r] = valid ? part * a.sl2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: per-query max and sum over the chunk (one wave per query)
+  for (int qi = wave; qi < nq; qi += 4) {
+    float m = -INFINITY;
+    for (int i = lane; i < n; i += 64) m = fmaxf(m, sc[qi][i]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float l = 0.f;
+    for (int i = lane; i < n; i += 64) {
+      const float p = __builtin_amdgcn_exp2f(sc[qi][i] - mu);
+      sc[qi][i] = p;
+      l += p;
+    }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) l += __shfl_xor(l, x);
+    if (lane == 0) {
+      ml[qi][0] = m;
+      ml[qi][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: acc[q][d] = sum_r p[q][r] v[r][d]
+  float acc[kMaxQ][8];
+#pragma unroll
+  for (int qi = 0; qi < kMaxQ; ++qi)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
+  for (int r0 = 0; r0 < n; r0 += RPR) {
+    const int r = r0 + grp;
+    if (r < n) {
+      float vx[8];
+      load8<F32>(vb + ((c0 + r) * a.k_sr + sub * 8) * ES, vx);
+#pragma unroll
+      for (int qi = 0; qi < kMaxQ; ++qi) {
+        if (qi < nq) {
+          const float p = sc[qi][r];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[qi][e] = fmaf(p, vx[e], acc[qi][e]);
+        }
+      }
+    }
+  }
+  // reduce over the row groups of this wave (lanes with equal sub)
+#pragma unroll
+  for (int qi = 0; qi < kMaxQ; ++qi)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[qi][e];
+#pragma unroll
+      for (int s = LPR; s < 64; s <<= 1) x += __shfl_xor(x, s);
+      acc[qi][e] = x;
+    }
+  if (lane < LPR)
+    for (int qi = 0; qi < nq; ++qi)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][qi][sub * 8 + e] = acc[qi][e];
+  __syncthreads();
+
+  // ---- write the partial state: [B][NKV][NQ_total][S] x (D acc, m, l)
+  const int nq_tot = a.NQ;
+  for (int i = tid; i < nq * D; i += 256) {
+    const int qi = i / D, d = i % D;
+    const float s = red[0][qi][d] + red[1][qi][d] + red[2][qi][d] + red[3][qi][d];
+    const long long slot = (((long long)b * a.NKV + kvh) * nq_tot + q_off + qi) * a.S + split;
+    a.ws[slot * (D + 2) + d] = s;
+  }
+  if (tid < nq) {
+    const long long slot = (((long long)b * a.NKV + kvh) * nq_tot + q_off + tid) * a.S + split;
+    a.ws[slot * (D + 2) + D] = ml[tid][0];
+    a.ws[slot * (D + 2) + D + 1] = ml[tid][1];
+  }
+}
+
+// One workgroup of D threads per (query, kv head, batch).
+template <int D, bool F32, bool DECODE>
+__global__ __launch_bounds__(128) void combine_kernel(const SplitArgs a, const GlobalList gl, int G) {
+  const int qi = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int d = threadIdx.x;
+  const long long base = (((long long)b * a.NKV + kvh) * a.NQ + qi) * a.S;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.ws[(base + s) * (D + 2) + D]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float *p = a.ws + (base + s) * (D + 2);
+    const float w = __builtin_amdgcn_exp2f(p[D] - Mu);
+    L = fmaf(w, p[D + 1], L);
+    acc = fmaf(w, p[d], acc);
+  }
+  const float out = (L > 0.f) ? acc / L : 0.f;
+  long long row;  // output row offset
+  if constexpr (DECODE) row = b * a.o_sb + kvh * a.o_sh + (long long)qi * a.o_sq;
+  else row = b * a.o_sb + kvh * a.o_sh + (long long)gl.idx[b * G + qi] * a.o_sq;
+  if constexpr (F32) static_cast<float *>(a.o)[row + d] = out;
+  else {
+    const __bf16 h = (__bf16)out;
+    static_cast<uint16_t *>(a.o)[row + d] = __builtin_bit_cast(uint16_t, h);
+  }
+  if (a.lse && d == 0) {
+    const float lse = (L > 0.f) ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+    if constexpr (DECODE) a.lse[((long long)b * a.NKV + kvh) * a.NQ + qi] = lse;
+    else {
+      // lse layout [B][H][T]; n_keys == T for global rows
+      a.lse[((long long)b * a.NKV + kvh) * a.n_keys + gl.idx[b * G + qi]] = lse;
+    }
+  }
+}
+
+template <int D, bool F32, bool DECODE>
+hipError_t run(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) {
+  dim3 grid(a.S, a.NKV, a.B);
+  for (int q0 = 0; q0 < a.NQ; q0 += kMaxQ) {
+    const int nq = min(kMaxQ, a.NQ - q0);
+    hipLaunchKernelGGL((split_kernel<D, F32, DECODE>), grid, dim3(256), 0, st, a, *gl, q0, nq, G);
+  }
+  hipLaunchKernelGGL((combine_kernel<D, F32, DECODE>), dim3(a.NQ, a.NKV, a.B), dim3(D), 0, st, a,
+                     *gl, G);
+  return hipGetLastError();
+}
+
+__global__ void cache_write_kernel(const char *kn, const char *vn, const int *pos, char *kc,
+                                   char *vc, int *slot_pos, int W, int Hkv, int row_bytes) {
+  const int b = blockIdx.y, hk = blockIdx.x;
+  const int p = pos[b];
+  if (p < 0) return;  // documented precondition; never index with a negative slot
+  const int slot = p % W;
+  const long long src = ((long long)b * Hkv + hk) * row_bytes;
+  const long long dst = (((long long)b * Hkv + hk) * W + slot) * row_bytes;
+  for (int i = threadIdx.x * 4; i < row_bytes; i += blockDim.x * 4) {
+    *reinterpret_cast<uint32_t *>(kc + dst + i) = *reinterpret_cast<const uint32_t *>(kn + src + i);
+    *reinterpret_cast<uint32_t *>(vc + dst + i) = *reinterpret_cast<const uint32_t *>(vn + src + i);
+  }
+  if (hk == 0 && threadIdx.x == 0) slot_pos[(long long)b * W + slot] = p;
+}
+
+__global__ void debug_mask_kernel(int mode, int T, int w_or_r, int dil, const GlobalList gl, int G,
+                                  uint8_t *mask) {
+  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (i >= (long long)T * T) return;
+  const int t = (int)(i / T), s = (int)(i % T);
+  bool on;
+  if (mode == SWA_MODE_CAUSAL) {
+    on = causal_in(t, s, w_or_r);
+  } else {
+    bool t_glob = false, s_glob = false;
+    for (int g = 0; g < G; ++g) {
+      t_glob |= gl.idx[g] == t;
+      s_glob |= gl.idx[g] == s;
+    }
+    on = t_glob || s_glob || dilated_in(t, s, w_or_r, dil);
+  }
+  mask[i] = on ? 1 : 0;
+}
+
+}  // namespace
+
+hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const GlobalList *gl,
+                        int G, int H, hipStream_t st) {
+  (void)H;
+  if (decode) {
+    if (f32) return D == 128 ? run<128, true, true>(a, gl, G, st) : run<64, true, true>(a, gl, G, st);
+    return D == 128 ? run<128, false, true>(a, gl, G, st) : run<64, false, true>(a, gl, G, st);
+  }
+  if (f32) return D == 128 ? run<128, true, false>(a, gl, G, st) : run<64, true, false>(a, gl, G, st);
+  return D == 128 ? run<128, false, false>(a, gl, G, st) : run<64, false, false>(a, gl, G, st);
+}
+
+int split_max_chunk() { return kMaxChunk; }
+
+hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
+                              void *vc, int *slot_pos, int B, int W, int Hkv, int D,
+                              hipStream_t st) {
+  const int row_bytes = D * (f32 ? 4 : 2);
+  hipLaunchKernelGGL(cache_write_kernel, dim3(Hkv, B), dim3(64), 0, st,
+                     static_cast<const char *>(kn), static_cast<const char *>(vn), pos,
+                     static_cast<char *>(kc), static_cast<char *>(vc), slot_pos, W, Hkv, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_mask(int mode, int T, int w_or_r, int dil, const GlobalList *gl, int G,
+                             uint8_t *mask, hipStream_t st) {
+  const long long n = (long long)T * T;
+  const int blocks = (int)((n + 255) / 256);
+  hipLaunchKernelGGL(debug_mask_kernel, dim3(blocks), dim3(256), 0, st, mode, T, w_or_r, dil, *gl,
+                     G, mask);
+  return hipGetLastError();
+}
+
+}  // namespace swa

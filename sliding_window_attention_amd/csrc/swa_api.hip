@@ -1,0 +1,293 @@
+// swa_api.hip — the C ABI of libswa.so (declared in include/swa.h).
+//
+// Every entry point validates all arguments on the host, then launches the
+// gfx950 kernels asynchronously on the caller's stream.  Nothing is allocated
+// and no state is kept between calls.
+//
+// Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
+// [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive);
+// [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com);
+// [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai).
+
+#include <cmath>
+#include <cstring>
+
+#include "swa_internal.h"
+
+namespace swa {
+
+int split_max_chunk();
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool dt_ok(swa_dtype dt) { return dt == SWA_BF16 || dt == SWA_F32; }
+bool d_ok(int d) { return d == 64 || d == 128; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Number of key chunks for a split-KV launch: enough workgroups to fill the
+// chip (>= 2048), chunks between 64 and the kernel's maximum.
+int choose_splits(long long heads_total, int n_keys) {
+  const int maxc = split_max_chunk();
+  int s_min = (n_keys + maxc - 1) / maxc;
+  int s_max = (n_keys + 63) / 64;
+  long long want = (2048 + heads_total - 1) / heads_total;
+  int s = (int)std::max<long long>(s_min, std::min<long long>(want, s_max));
+  if (s < 1) s = 1;
+  const int chunk = (n_keys + s - 1) / s;
+  return (n_keys + chunk - 1) / chunk;
+}
+
+swa_status hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
+
+}  // namespace
+}  // namespace swa
+
+using namespace swa;
+
+extern "C" {
+
+const char *swa_status_str(swa_status s) {
+  switch (s) {
+    case SWA_OK: return "ok";
+    case SWA_ERR_INVALID: return "invalid argument";
+    case SWA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SWA_ERR_WORKSPACE: return "workspace too small";
+    case SWA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int swa_version(void) { return 1; }
+
+swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *BN) {
+  if (!BM || !BN || H_q < 1 || H_kv < 1 || H_q % H_kv) return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  if (entry == 'p') {
+    *BM = kRowsPerWave * kWaves / prefill_pack(H_q, H_kv);
+  } else if (entry == 'l') {
+    *BM = kRowsPerWave * kWaves;
+  } else {
+    return SWA_ERR_INVALID;
+  }
+  *BN = kBN;
+  return SWA_OK;
+}
+
+int swa_band_tiles(int mode, int T, int w_or_r, int BM, int BN, int32_t *out, int cap) {
+  if (T < 1 || BM < 1 || BN < 1 || cap < 0 || (cap > 0 && !out)) return -1;
+  if (mode == SWA_MODE_CAUSAL ? w_or_r < 1 : (mode == SWA_MODE_SYMMETRIC ? w_or_r < 0 : true))
+    return -1;
+  int n = 0;
+  const int nq = (T + BM - 1) / BM;
+  for (int qi = 0; qi < nq; ++qi) {
+    const int t0 = qi * BM, t1 = std::min(T, t0 + BM) - 1;
+    const TileRange tr = mode == SWA_MODE_CAUSAL ? causal_tile_range(t0, t1, w_or_r, BN)
+                                                 : sym_tile_range(t0, t1, w_or_r, T, BN);
+    for (int kj = tr.lo; kj <= tr.hi; ++kj) {
+      const bool full = mode == SWA_MODE_CAUSAL ? causal_tile_full(t0, t1, kj, BN, w_or_r, T)
+                                                : sym_tile_full(t0, t1, kj, BN, w_or_r, T);
+      if (n < cap) {
+        out[3 * n] = qi;
+        out[3 * n + 1] = kj;
+        out[3 * n + 2] = full ? 0 : 1;
+      }
+      ++n;
+    }
+  }
+  return n;
+}
+
+swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int T, int H_q, int H_kv, int d_h, int W, float scale,
+                       void *stream) {
+  if (!dt_ok(dt) || !q || !k || !v || !o) return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || T < 1 || H_q < 1 || H_kv < 1 || W < 1 || H_q % H_kv || !scale_ok(scale))
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.T = T; a.Hq = H_q; a.Hkv = H_kv;
+  a.q_st = (long long)H_q * d_h;
+  a.q_sb = a.q_st * T;
+  a.k_st = (long long)H_kv * d_h;
+  a.k_sb = a.k_st * T;
+  a.W = W;
+  a.sl2 = scale * kLog2e;
+  a.group = H_q / H_kv;
+  a.P = prefill_pack(H_q, H_kv);
+  a.BM = kRowsPerWave * kWaves / a.P;
+  a.n_qt = (T + a.BM - 1) / a.BM;
+  a.n_hg = H_q / a.P;
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, false, d_h, &gl, st));
+  if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL) return SWA_ERR_UNSUPPORTED;
+  return hip_status(launch_fwd_bf16(a, false, d_h, &gl, st));
+}
+
+size_t swa_decode_workspace_size(int B, int H_q, int H_kv, int W, int d_h) {
+  if (B < 1 || H_q < 1 || H_kv < 1 || W < 1 || H_q % H_kv || !d_ok(d_h)) return 0;
+  const int S = choose_splits((long long)B * H_kv, W);
+  return (size_t)B * H_q * S * (d_h + 2) * sizeof(float);
+}
+
+swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *slot_pos, const int32_t *cur_pos, void *o, float *lse,
+                      int B, int W, int H_q, int H_kv, int d_h, float scale, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!dt_ok(dt) || !q || !k_cache || !v_cache || !slot_pos || !cur_pos || !o)
+    return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(slot_pos, 4) || !aligned(cur_pos, 4) || (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || W < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || !scale_ok(scale))
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  const size_t need = swa_decode_workspace_size(B, H_q, H_kv, W, d_h);
+  if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SWA_ERR_INVALID;
+
+  SplitArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.ws = static_cast<float *>(workspace);
+  a.slot_pos = slot_pos; a.cur_pos = cur_pos;
+  a.B = B; a.NKV = H_kv; a.NQ = H_q / H_kv;
+  a.n_keys = W;
+  a.S = choose_splits((long long)B * H_kv, W);
+  a.chunk = (W + a.S - 1) / a.S;
+  a.W = W;
+  a.q_sq = d_h; a.q_sh = (long long)a.NQ * d_h; a.q_sb = (long long)H_q * d_h;
+  a.o_sq = a.q_sq; a.o_sh = a.q_sh; a.o_sb = a.q_sb;
+  a.k_sr = d_h; a.k_sh = (long long)W * d_h; a.k_sb = (long long)H_kv * W * d_h;
+  a.sl2 = scale * kLog2e;
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  return hip_status(launch_split(a, true, dt == SWA_F32, d_h, &gl, 0, H_kv,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new, const int32_t *pos,
+                           void *k_cache, void *v_cache, int32_t *slot_pos, int B, int W, int H_kv,
+                           int d_h, void *stream) {
+  if (!dt_ok(dt) || !k_new || !v_new || !pos || !k_cache || !v_cache || !slot_pos)
+    return SWA_ERR_INVALID;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(pos, 4) || !aligned(slot_pos, 4))
+    return SWA_ERR_INVALID;
+  if (B < 1 || W < 1 || H_kv < 1) return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  return hip_status(launch_cache_write(dt == SWA_F32, k_new, v_new, pos, k_cache, v_cache,
+                                       slot_pos, B, W, H_kv, d_h,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t swa_longformer_workspace_size(int B, int T, int H, int d_h, int G) {
+  if (B < 1 || T < 1 || H < 1 || G < 0 || !d_ok(d_h)) return 0;
+  if (G == 0) return 0;
+  const int S = choose_splits((long long)B * H, T);
+  return (size_t)B * H * G * S * (d_h + 2) * sizeof(float);
+}
+
+swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                          float *lse, int B, int T, int H, int d_h, int r, const int32_t *dilation,
+                          const int32_t *global_idx, int G, float scale, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (!dt_ok(dt) || !q || !k || !v || !o) return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || T < 1 || H < 1 || r < 0 || G < 0 || !scale_ok(scale)) return SWA_ERR_INVALID;
+  if ((G > 0) != (global_idx != nullptr)) return SWA_ERR_INVALID;
+  if (dilation)
+    for (int h = 0; h < H; ++h)
+      if (dilation[h] < 1 || dilation[h] > 65535) return SWA_ERR_INVALID;
+  for (int b = 0; b < B && G > 0; ++b)
+    for (int g = 0; g < G; ++g) {
+      const int x = global_idx[b * G + g];
+      if (x < 0 || x >= T || (g > 0 && x <= global_idx[b * G + g - 1])) return SWA_ERR_INVALID;
+    }
+  if (!d_ok(d_h) || H > kMaxHeadsLF || (long long)B * G > kMaxGlobalsLF) return SWA_ERR_UNSUPPORTED;
+  const size_t need = (dt == SWA_F32) ? 0 : swa_longformer_workspace_size(B, T, H, d_h, G);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SWA_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return SWA_ERR_INVALID;
+
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.T = T; a.Hq = H; a.Hkv = H;
+  a.q_st = (long long)H * d_h;
+  a.q_sb = a.q_st * T;
+  a.k_st = a.q_st;
+  a.k_sb = a.q_sb;
+  a.W = r;
+  a.sl2 = scale * kLog2e;
+  a.group = 1;
+  a.P = 1;
+  a.BM = kRowsPerWave * kWaves;
+  a.G = G;
+  long long tiles = 0;
+  for (int h = 0; h < H; ++h) {
+    const int d = dilation ? dilation[h] : 1;
+    a.dil[h] = (unsigned short)d;
+    a.head_off[h] = (int)tiles;
+    tiles += class_tiles(T, d, a.BM);
+  }
+  a.head_off[H] = (int)tiles;
+  if (tiles * B > 0x7fffffffLL) return SWA_ERR_UNSUPPORTED;
+  a.tiles_per_batch = (int)tiles;
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  for (int i = 0; i < B * G; ++i) gl.idx[i] = global_idx[i];
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, true, d_h, &gl, st));
+
+  hipError_t e = launch_fwd_bf16(a, true, d_h, &gl, st);
+  if (e != hipSuccess || G == 0) return hip_status(e);
+  // Global rows attend every position: split-KV over all T keys, written after
+  // (stream order) the local pass, replacing those rows.
+  SplitArgs s;
+  std::memset(&s, 0, sizeof(s));
+  s.q = q; s.k = k; s.v = v; s.o = o; s.lse = lse;
+  s.ws = static_cast<float *>(workspace);
+  s.B = B; s.NKV = H; s.NQ = G;
+  s.n_keys = T;
+  s.S = choose_splits((long long)B * H, T);
+  s.chunk = (T + s.S - 1) / s.S;
+  s.q_sb = a.q_sb; s.q_sh = d_h; s.q_sq = a.q_st;
+  s.o_sb = a.q_sb; s.o_sh = d_h; s.o_sq = a.q_st;
+  s.k_sb = a.k_sb; s.k_sh = d_h; s.k_sr = a.k_st;
+  s.sl2 = a.sl2;
+  return hip_status(launch_split(s, false, false, d_h, &gl, G, H, st));
+}
+
+swa_status swa_debug_index_mask(int mode, int T, int w_or_r, int dil, const int32_t *global_idx,
+                                int G, uint8_t *mask_dev, void *stream) {
+  if (!mask_dev || T < 1 || G < 0 || (G > 0 && !global_idx)) return SWA_ERR_INVALID;
+  if (mode == SWA_MODE_CAUSAL) {
+    if (w_or_r < 1 || G != 0) return SWA_ERR_INVALID;
+  } else if (mode == SWA_MODE_SYMMETRIC) {
+    if (w_or_r < 0 || dil < 1) return SWA_ERR_INVALID;
+  } else {
+    return SWA_ERR_INVALID;
+  }
+  if ((long long)T * T > (1LL << 31) || G > kMaxGlobalsLF) return SWA_ERR_UNSUPPORTED;
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  for (int g = 0; g < G; ++g) {
+    if (global_idx[g] < 0 || global_idx[g] >= T) return SWA_ERR_INVALID;
+    gl.idx[g] = global_idx[g];
+  }
+  return hip_status(launch_debug_mask(mode, T, w_or_r, mode == SWA_MODE_CAUSAL ? 1 : dil, &gl, G,
+                                      mask_dev, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// swa_internal.h — definitions shared by the host launchers and the gfx950 kernels.
+//
+// The window predicates and the band-tile schedule are written once here as
+// __host__ __device__ functions: the kernels run them, and swa_band_tiles /
+// swa_debug_index_mask export exactly the same code for testing.
+//
+// Page tags used in comments:
+//   [KB] "Sliding Window Attention", LLM architecture knowledge base (lizeman.github.io)
+//   [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive.pages.dev)
+//   [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com)
+//   [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/swa.h"
+
+namespace swa {
+
+// ---------------------------------------------------------------- predicates
+
+// Causal window ([KB] §2 N_t, §3 mask): key s is attended by query t iff t-W < s <= t.
+__host__ __device__ inline bool causal_in(int t, int s, int W) { return s <= t && s > t - W; }
+
+// Undilated symmetric window in one residue class ([PP] §1.1): |i - j| <= r.
+__host__ __device__ inline bool sym_in(int i, int j, int r) {
+  const int d = i - j;
+  return d <= r && -d <= r;
+}
+
+// Dilated window on original positions ([PP] §3.1): j = i + k*dil with |k| <= r.
+__host__ __device__ inline bool dilated_in(int i, int j, int r, int dil) {
+  const int d = i - j;
+  if (d % dil != 0) return false;
+  const int k = d / dil;
+  return k <= r && -k <= r;
+}
+
+// ---------------------------------------------------------------- band tiles
+//
+// A query tile holds the valid rows [t0, t1]; key tiles have BN columns.  The
+// visited key tiles form the contiguous range [lo, hi] (every tile in it holds
+// at least one attended pair); a visited tile needs a mask unless every pair
+// of valid rows x columns in it is attended (columns >= n count as masked).
+
+struct TileRange {
+  int lo, hi;
+};
+
+__host__ __device__ inline TileRange causal_tile_range(int t0, int t1, int W, int BN) {
+  int s_lo = t0 - W + 1;
+  if (s_lo < 0) s_lo = 0;
+  return {s_lo / BN, t1 / BN};
+}
+
+__host__ __device__ inline bool causal_tile_full(int t0, int t1, int kj, int BN, int W, int n) {
+  const int s0 = kj * BN, s1 = s0 + BN - 1;
+  return s1 <= t0 && s0 > t1 - W && s1 < n;
+}
+
+__host__ __device__ inline TileRange sym_tile_range(int i0, int i1, int r, int n, int BN) {
+  int s_lo = i0 - r;
+  if (s_lo < 0) s_lo = 0;
+  int s_hi = i1 + r;
+  if (s_hi > n - 1) s_hi = n - 1;
+  return {s_lo / BN, s_hi / BN};
+}
+
+__host__ __device__ inline bool sym_tile_full(int i0, int i1, int kj, int BN, int r, int n) {
+  const int s0 = kj * BN, s1 = s0 + BN - 1;
+  return s1 - i0 <= r && i1 - s0 <= r && s1 < n;
+}
+
+// ---------------------------------------------------------------- residue classes
+//
+// A head with dilation dil splits positions into dil classes rho = i mod dil;
+// within a class the dilated window is an undilated window of radius r on the
+// subsequence rho, rho+dil, ... ([PP] §3.1-3.2: keys i + k*dil stay in i's class).
+struct ClassSplit {
+  int q, rem;  // n = q*dil + rem; classes rho < rem have length q+1, others q
+};
+__host__ __device__ inline ClassSplit class_split(int n, int dil) { return {n / dil, n % dil}; }
+__host__ __device__ inline int class_len(ClassSplit c, int rho) { return c.q + (rho < c.rem ? 1 : 0); }
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// Number of BM-row query tiles a head with dilation dil needs over all its classes.
+__host__ __device__ inline int class_tiles(int n, int dil, int BM) {
+  const ClassSplit c = class_split(n, dil);
+  return c.rem * ceil_div(c.q + 1, BM) + (dil - c.rem) * ceil_div(c.q, BM);
+}
+// Inverse of the enumeration above: tile index -> (class, tile within class).
+__host__ __device__ inline void class_tile_decode(int n, int dil, int BM, int idx, int *rho, int *tile) {
+  const ClassSplit c = class_split(n, dil);
+  const int c1 = ceil_div(c.q + 1, BM), c0 = ceil_div(c.q, BM);
+  if (idx < c.rem * c1) {
+    *rho = idx / c1;
+    *tile = idx % c1;
+  } else {
+    idx -= c.rem * c1;
+    *rho = c.rem + idx / c0;
+    *tile = idx % c0;
+  }
+}
+
+// ---------------------------------------------------------------- launch geometry
+
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each
+// with its own L2.  Remap so that every XCD owns one contiguous range of
+// logical ids (neighbouring query tiles of the same head share K/V in that L2).
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  constexpr int NX = 8;
+  const int q = nblocks / NX, rem = nblocks % NX;
+  const int x = bid % NX, idx = bid / NX;
+  return x * q + (x < rem ? x : rem) + idx;
+}
+
+constexpr int kBN = 64;          // key tile (columns) of the bf16 MFMA kernels
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kRowsPerWave = 32; // query rows per wave (one 32x32 MFMA block)
+
+// Heads packed into one workgroup for the causal kernel: waves of one
+// workgroup take query heads that share a key/value head, so a staged K/V tile
+// serves several heads ([ST] "Combining SWA with GQA": query heads share one
+// key/value head).
+inline int prefill_pack(int H_q, int H_kv) {
+  const int g = H_q / H_kv;
+  return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+}
+
+// ---------------------------------------------------------------- kernel arguments
+
+constexpr int kMaxHeadsLF = 256;
+constexpr int kMaxGlobalsLF = 512;
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int B, T, Hq, Hkv;
+  long long q_sb, q_st;  // element strides of q/o: batch, token (head stride = D)
+  long long k_sb, k_st;  // element strides of k/v
+  int W;                 // causal window, or radius r in symmetric mode
+  float sl2;             // scale * log2(e)
+  int P, group;          // heads per workgroup, H_q / H_kv
+  int n_qt, n_hg;        // causal: query tiles per head group, head groups
+  int BM;                // query rows per workgroup
+  // symmetric (Longformer) mode
+  int G;                       // globals per batch row
+  int tiles_per_batch;         // sum over heads of class tiles
+  int head_off[kMaxHeadsLF + 1];   // prefix sums of class tiles per head
+  unsigned short dil[kMaxHeadsLF]; // per-head dilation
+};
+
+struct GlobalList {
+  int idx[kMaxGlobalsLF];  // [B][G] positions
+};
+
+// Split-KV attention for few queries against many keys (ring decode, and the
+// global rows of Longformer attention, which attend every position).
+struct SplitArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  float *ws;  // partials: [B][NH][NQ][S] x (D acc, m, l)
+  const int *slot_pos, *cur_pos;  // decode mode
+  int B, NKV, NQ;        // batch, key/value heads, queries per kv head
+  int n_keys, chunk, S;  // keys per (b, kv head), keys per split, splits
+  int W;                 // decode window
+  long long q_sb, q_sh, q_sq;     // q strides: batch, kv head, query-in-group
+  long long k_sb, k_sh, k_sr;     // k/v strides: batch, head, key row
+  long long o_sb, o_sh, o_sq;     // o strides
+  float sl2;
+};
+
+// ---------------------------------------------------------------- launchers (host)
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+                           hipStream_t st);
+hipError_t launch_fwd_f32(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+                          hipStream_t st);
+hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const GlobalList *gl,
+                        int G, int H, hipStream_t st);
+hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
+                              void *vc, int *slot_pos, int B, int W, int Hkv, int D,
+                              hipStream_t st);
+hipError_t launch_debug_mask(int mode, int T, int w_or_r, int dil, const GlobalList *gl, int G,
+                             uint8_t *mask, hipStream_t st);
+
+}  // namespace swa

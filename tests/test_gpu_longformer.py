@@ -1,0 +1,125 @@
+"""GPU parity: swa_longformer (symmetric window, dilation, global tokens) and the
+device-side window predicate, against the oracle."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sliding_window_attention_amd import binding as bd
+from sliding_window_attention_amd import inputs as inp
+from gpu_util import TOL_BF16, TOL_F32, TOL_LSE_BF16, TOL_LSE_F32, banner, dev, host, max_err
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# B, T, H, D, r, dilation, globals
+SMALL = [
+    (1, 16, 1, 64, 2, [1], []),
+    (1, 16, 2, 64, 2, [1, 2], [[0, 8]]),
+    (2, 300, 4, 64, 20, [1, 2, 3, 1], [[0, 77], [5, 299]]),
+    (2, 300, 4, 128, 20, [1, 2, 3, 1], [[10, 11], [0, 1]]),
+    (1, 257, 3, 64, 0, [1, 2, 5], [[128]]),
+    (1, 200, 2, 64, 300, [1, 2], []),
+    (2, 520, 4, 64, 64, [1, 1, 2, 2], [[0, 8], [200, 519]]),
+    (1, 129, 2, 128, 63, [4, 1], [[3, 64, 65, 100]]),
+    (1, 90, 2, 64, 5, [100, 1], [[0]]),
+]
+
+
+def _run(case, dtype):
+    B, T, H, D, r, dil, gl = case
+    c = inp.LongformerCase(B=B, T=T, H=H, D=D, r=r, dilation=dil,
+                           globals_=gl[0] if gl else [], dtype=dtype, seed=T + 7 * H)
+    q, k, v, dl, _ = inp.longformer_inputs(c)
+    g = np.asarray(gl, dtype=np.int32).reshape(B, -1) if gl else None
+    if g is not None and g.shape[0] != B:
+        g = np.repeat(g, B, axis=0)
+    banner(f"longformer {dtype} {case}")
+    o, lse = bd.longformer(dev(q), dev(k), dev(v), r, dl, g, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.swa_longformer(inp.widen(q), inp.widen(k), inp.widen(v), r, dl, g)
+    return host(o), host(lse), ro, rl
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c[:5]) for c in SMALL])
+def test_longformer_bf16(case):
+    o, lse, ro, rl = _run(case, "bf16")
+    assert max_err(o, ro) <= TOL_BF16
+    assert max_err(lse, rl) <= TOL_LSE_BF16
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c[:5]) for c in SMALL])
+def test_longformer_f32(case):
+    o, lse, ro, rl = _run(case, "f32")
+    assert max_err(o, ro) <= TOL_F32
+    assert max_err(lse, rl) <= TOL_LSE_F32
+
+
+def test_small_symmetric_workload_fp32():
+    # n=16, r=2, d_h=64, float32, one head: the running example's shape
+    c = inp.C1
+    q, k, v, dl, _ = inp.longformer_inputs(c)
+    banner("longformer n16 r2 fp32")
+    o = host(bd.longformer(dev(q), dev(k), dev(v), c.r, dl, None))
+    ro, _ = oracle.swa_longformer(inp.widen(q), inp.widen(k), inp.widen(v), c.r, dl, None)
+    assert max_err(o, ro) <= TOL_F32
+
+
+def _readout(dtype, r, dil, glist, n=16, D=64):
+    q = torch.zeros(1, n, 1, D)
+    k = torch.from_numpy(inp.normal((1, n, 1, D), 21))
+    v = torch.zeros(1, n, 1, D)
+    for s in range(n):
+        v[0, s, 0, s] = 1.0
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = np.asarray([glist], dtype=np.int32) if glist else None
+    o = host(bd.longformer(dev(q.to(tdt)), dev(k.to(tdt)), dev(v.to(tdt)), r, [dil], g))
+    return o[0, :, 0]
+
+
+def _table(name):
+    rows = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#") and not line.startswith("total"):
+            i, vals = line.split(":")
+            rows[int(i)] = [int(x) for x in vals.split()]
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name,r,dil,gl,total", [
+    ("pp_symmetric_n16_r2.txt", 2, 1, [], 74),
+    ("pp_dilated_n16_r2_d2.txt", 2, 2, [], 68),
+    ("pp_global_n16_r2_G0_8.txt", 2, 1, [0, 8], 120),
+])
+def test_index_readout_printed_tables(dtype, name, r, dil, gl, total):
+    # q = 0 and one-hot v read the kernels' connectivity sets out exactly; they
+    # must be the printed tables, row by row, and sum to the printed totals.
+    banner(f"longformer readout {dtype} {name}")
+    o = _readout(dtype, r, dil, gl)
+    table = _table(name)
+    count = 0
+    for i in range(16):
+        sup = np.nonzero(o[i])[0].tolist()
+        count += len(sup)
+        assert sup == oracle.longformer_index_set(i, 16, r, dil, gl).tolist()
+        if i in table:
+            assert sup == table[i]
+        np.testing.assert_allclose(o[i][sup], 1.0 / len(sup), rtol=2 ** -8)
+    assert count == total
+
+
+@pytest.mark.parametrize("mode,T,w,dil,gl", [
+    (0, 300, 70, 1, []), (0, 257, 1, 1, []), (0, 100, 500, 1, []),
+    (1, 300, 20, 1, []), (1, 300, 20, 3, [0, 77, 299]), (1, 257, 64, 2, [128]),
+    (1, 16, 2, 2, []), (1, 16, 2, 1, [0, 8]),
+])
+def test_device_predicate_matches_oracle(mode, T, w, dil, gl):
+    banner(f"debug mask mode={mode} T={T} w={w} dil={dil}")
+    m = bd.debug_index_mask(mode, T, w, dil, gl).cpu().numpy().astype(bool)
+    want = oracle.causal_mask(T, w) if mode == 0 else oracle.longformer_mask(T, w, dil, gl)
+    assert np.array_equal(m, want)
