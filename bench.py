@@ -1,0 +1,220 @@
+"""Throughput of the sliding-window attention forward pass on one MI355X.
+
+One JSON line on stdout.  The headline is causal prefill at T=16384,
+W=4096, H_q=32, H_kv=8, d_h=128, bf16 (band-TFLOP/s: 4*d_h FLOP per attended
+(query head, key) pair, masked tile work excluded).  The other workloads
+(causal prefill B=2 T=32768 W=1024 local-layer shape, ring decode B=64 W=4096,
+Longformer B=8 T=4096 r=256) are reported in "extra".
+
+Timing: inputs resident in HBM, W untimed warm-up launches, then K launches
+bracketed by torch.cuda.synchronize() and HIP events recorded on the stream the
+kernels are launched on (torch's current stream, which the binding passes to
+the library).
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--only prefill] [--profile-copy]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sliding_window_attention_amd import binding as bd  # noqa: E402
+from sliding_window_attention_amd import inputs as inp  # noqa: E402
+
+METRIC = "SWA prefill band-TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def causal_pairs(T, W):
+    """Attended (query, key) pairs per head of a causal window: sum_t min(t+1, W)."""
+    w = min(W, T)
+    return T * w - w * (w - 1) // 2
+
+
+def longformer_pairs(T, r, dil, globals_):
+    """Attended pairs per batch row, summed over heads, counted directly from the
+    window bounds (global rows attend all T; other rows add the globals outside
+    their window)."""
+    G = np.asarray(sorted(globals_), dtype=np.int64)
+    i = np.arange(T, dtype=np.int64)
+    is_g = np.isin(i, G)
+    total = 0
+    for d in dil:
+        k_lo = np.maximum(-r, -(i // d))
+        k_hi = np.minimum(r, (T - 1 - i) // d)
+        win = k_hi - k_lo + 1
+        extra = np.zeros(T, dtype=np.int64)
+        for g in G:
+            diff = i - g
+            inside = (diff % d == 0) & (np.abs(diff) <= r * d)
+            extra += (~inside).astype(np.int64)
+        total += int(np.where(is_g, T, win + extra).sum())
+    return total
+
+
+def time_launches(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def bench_prefill(c, steps, warmup):
+    q, k, v = (x.cuda() for x in inp.prefill_inputs(c))
+    o = torch.empty_like(q)
+    ms, _ = time_launches(lambda: bd.prefill(q, k, v, c.W, out=o), steps, warmup)
+    flops = 4.0 * c.D * c.Hq * c.B * causal_pairs(c.T, c.W)
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel())
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(ms=ms, tflops=tflops, flops=flops, bytes=nbytes)
+
+
+def bench_decode(c, steps, warmup):
+    q, kc, vc, sp, cur = (x.cuda() for x in inp.decode_inputs(c))
+    o = torch.empty_like(q)
+    ws = torch.empty(bd.decode_workspace_size(c.B, c.Hq, c.Hkv, c.W, c.D), dtype=torch.uint8,
+                     device="cuda")
+    ms, _ = time_launches(lambda: bd.decode(q, kc, vc, sp, cur, out=o, workspace=ws), steps, warmup)
+    nbytes = 2 * (q.numel() + kc.numel() + vc.numel() + o.numel()) + 4 * (sp.numel() + cur.numel())
+    return dict(ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, bytes=nbytes)
+
+
+def bench_longformer(c, steps, warmup):
+    q, k, v, dl, g = inp.longformer_inputs(c)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(q)
+    ws = torch.empty(max(1, bd.longformer_workspace_size(c.B, c.T, c.H, c.D, g.shape[1])),
+                     dtype=torch.uint8, device="cuda")
+    ms, _ = time_launches(lambda: bd.longformer(q, k, v, c.r, dl, g, out=o, workspace=ws),
+                          steps, warmup)
+    pairs = c.B * longformer_pairs(c.T, c.r, c.dilation, c.globals_)
+    flops = 4.0 * c.D * pairs
+    nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel())
+    t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+    return dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12, pairs=pairs, bytes=nbytes,
+                frac_of_roof=t_roof / (ms * 1e-3))
+
+
+def cpu_baseline(c, budget_s=12.0):
+    """The fp64 oracle as it is, single-threaded, on steady-state rows of the
+    headline workload, all heads; scaled to band-TFLOP/s."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    q, k, v = inp.prefill_inputs(c)
+    qn, kn, vn = inp.widen(q), inp.widen(k), inp.widen(v)
+    rows_done, t_used = 0, 0.0
+    t_row = c.W + 100
+    with threadpool_limits(limits=1):
+        while t_used < budget_s and t_row < c.T:
+            t0 = time.perf_counter()
+            oracle.swa_prefill(qn, kn, vn, c.W, rows=[t_row])
+            t_used += time.perf_counter() - t0
+            rows_done += 1
+            t_row += 7
+    flops = 4.0 * c.D * c.Hq * c.W * rows_done
+    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=1, kind="oracle",
+                sample=f"{rows_done} steady-state query rows (t >= W, {c.W} keys each) x all "
+                       f"{c.Hq} heads of the T={c.T} W={c.W} workload, {t_used:.1f} s, "
+                       f"one thread (BLAS limited to 1)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill"], default="all")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the build has no multi-GPU path "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bd.lib()
+
+    if args.profile_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    c2 = inp.C2
+    main_r = bench_prefill(c2, args.steps, args.warmup)
+    extra = {}
+    if args.only == "all":
+        r3 = bench_prefill(inp.C3, max(5, args.steps // 2), args.warmup)
+        extra["prefill_local_layer"] = dict(
+            workload="causal SWA prefill B=2 T=32768 W=1024 Hq=32 Hkv=16 d_h=128 bf16, RoPE inputs",
+            value=round(r3["tflops"], 2), unit="TFLOP/s", ms=round(r3["ms"], 4),
+            frac_mfma_peak=round(r3["tflops"] / PEAK_BF16_TFLOPS, 4))
+        r4 = bench_decode(inp.C4, max(20, args.steps), args.warmup)
+        extra["decode"] = dict(
+            workload="ring decode B=64 W=4096 Hq=32 Hkv=8 d_h=128 bf16, cur_pos in [4096, 32768)",
+            value=round(r4["gbs"], 1), unit="GB/s", ms=round(r4["ms"], 4),
+            frac_hbm_peak=round(r4["gbs"] / PEAK_HBM_GBS, 4), bytes=r4["bytes"])
+        r5 = bench_longformer(inp.C5, max(20, args.steps), args.warmup)
+        extra["longformer"] = dict(
+            workload="Longformer B=8 T=4096 H=12 d_h=64 r=256, dilation 2 on heads 8-11, globals {0,8}",
+            value=round(r5["tflops"], 2), unit="TFLOP/s", ms=round(r5["ms"], 4),
+            frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(c2)
+
+    ach = main_r["tflops"]
+    out = {
+        "metric": METRIC,
+        "value": round(ach, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal SWA prefill (one launch per step)", "B": c2.B, "T": c2.T,
+                   "W": c2.W, "H_q": c2.Hq, "H_kv": c2.Hkv, "d_h": c2.D, "io": "bf16",
+                   "accumulate": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "fwd_kernel<128, causal>",
+                     "algorithmic_flop_per_launch": main_r["flops"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -108,7 +108,7 @@ def test_prefill_writes_only_output_and_is_deterministic():
     o2 = bd.prefill(q, k, v, 90)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
-    out = torch.full((2, 300, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((2, 1, 300, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     bd.prefill(q, k, v, 90, out=out[0])
     torch.cuda.synchronize()
     assert torch.equal(out[0], o1) and bool((out[1] == 7.0).all())
