@@ -146,7 +146,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "longformer", "local"],
+                    default="all", help="restrict to one workload (the headline always runs "
+                    "unless decode/longformer/local is chosen)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -165,25 +167,32 @@ def main():
         del src, dst
 
     c2 = inp.C2
-    main_r = bench_prefill(c2, args.steps, args.warmup)
+    main_r = None
+    if args.only in ("all", "prefill"):
+        main_r = bench_prefill(c2, args.steps, args.warmup)
     extra = {}
-    if args.only == "all":
+    if args.only in ("all", "local"):
         r3 = bench_prefill(inp.C3, max(5, args.steps // 2), args.warmup)
         extra["prefill_local_layer"] = dict(
             workload="causal SWA prefill B=2 T=32768 W=1024 Hq=32 Hkv=16 d_h=128 bf16, RoPE inputs",
             value=round(r3["tflops"], 2), unit="TFLOP/s", ms=round(r3["ms"], 4),
             frac_mfma_peak=round(r3["tflops"] / PEAK_BF16_TFLOPS, 4))
+    if args.only in ("all", "decode"):
         r4 = bench_decode(inp.C4, max(20, args.steps), args.warmup)
         extra["decode"] = dict(
             workload="ring decode B=64 W=4096 Hq=32 Hkv=8 d_h=128 bf16, cur_pos in [4096, 32768)",
             value=round(r4["gbs"], 1), unit="GB/s", ms=round(r4["ms"], 4),
             frac_hbm_peak=round(r4["gbs"] / PEAK_HBM_GBS, 4), bytes=r4["bytes"])
+    if args.only in ("all", "longformer"):
         r5 = bench_longformer(inp.C5, max(20, args.steps), args.warmup)
         extra["longformer"] = dict(
             workload="Longformer B=8 T=4096 H=12 d_h=64 r=256, dilation 2 on heads 8-11, globals {0,8}",
             value=round(r5["tflops"], 2), unit="TFLOP/s", ms=round(r5["ms"], 4),
             frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"])
 
+    if main_r is None:
+        print(json.dumps({"partial": args.only, "extra": extra}), flush=True)
+        return
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(c2)

@@ -222,6 +222,283 @@ __global__ __launch_bounds__(128) void combine_kernel(const SplitArgs a, const G
   }
 }
 
+// ---- bf16 path: one wave per (split, kv head, query pass, batch) ----------------
+//
+// Keys are walked in blocks of 32.  Per block:
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the A operand (K) is loaded from
+//         HBM straight into the operand layout (lane = key row, 16 bytes per
+//         k-step), Q^T (B operand) stays in VGPRs; only QG of the 32 query
+//         columns are live (the MFMA has ample headroom on an HBM-bound path);
+//   online softmax: each lane owns one query column, the block max / sum is a
+//         16-register reduction plus one v_permlane32_swap;
+//   O += P V on v_dot2_f32_bf16: lanes own 8 output columns of one row group;
+//         rows are paired so each lane reads the pair's two P values as one
+//         packed dword from LDS.
+// The next block's K/V loads are issued before the current block is computed.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ inline float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xhalf_add(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline uint32_t pack2_bf16(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int D>
+struct DecBlock {
+  static constexpr int KS = D / 16;    // MFMA k-steps over d_h
+  static constexpr int TPR = D / 8;    // lanes per V row (16 bytes each)
+  static constexpr int RG = 64 / TPR;  // V row groups per wave
+  static constexpr int RPL = 32 / RG;  // V rows per lane per block
+  U4 k[KS];
+  U4 v[RPL];
+  int valid;                           // this lane's key (lane & 31) is attended
+};
+
+template <int D>
+__device__ inline void dec_load_k(DecBlock<D> &blk, const uint16_t *kbase, const SplitArgs &a,
+                                  int s0, int c1, int lane) {
+  using Bk = DecBlock<D>;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int sk = s0 + lq;
+  if (sk < c1) {
+    const uint16_t *kr = kbase + (long long)sk * a.k_sr + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < Bk::KS; ++ks) blk.k[ks] = *reinterpret_cast<const U4 *>(kr + ks * 16);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < Bk::KS; ++ks) blk.k[ks] = U4{{0, 0, 0, 0}};
+  }
+}
+
+template <int D, bool DECODE>
+__device__ inline int dec_valid(const SplitArgs &a, int b, int s0, int c1, int cur, int lane) {
+  const int sk = s0 + (lane & 31);
+  int ok = sk < c1;
+  if constexpr (DECODE) {
+    if (ok) {
+      const int p = a.slot_pos[(long long)b * a.n_keys + sk];
+      ok = p >= 0 && p > cur - a.W && p <= cur;
+    }
+  }
+  return ok;
+}
+
+template <int D>
+__device__ inline void dec_load_v(DecBlock<D> &blk, const uint16_t *vbase, const SplitArgs &a,
+                                  int s0, int c1, int lane) {
+  using Bk = DecBlock<D>;
+  const int g = lane / Bk::TPR, c = lane % Bk::TPR;
+#pragma unroll
+  for (int i = 0; i < Bk::RPL; ++i) {
+    const int sv = s0 + Bk::RG * i + g;
+    if (sv < c1) blk.v[i] = *reinterpret_cast<const U4 *>(vbase + (long long)sv * a.k_sr + c * 8);
+    else blk.v[i] = U4{{0, 0, 0, 0}};
+  }
+}
+
+template <int D, int QG, bool DECODE>
+__global__ __launch_bounds__(64, QG >= 8 ? 1 : 2) void split_mfma_kernel(const SplitArgs a, const GlobalList gl,
+                                                        int G, int n_pass) {
+  using Bk = DecBlock<D>;
+  constexpr int KS = Bk::KS, TPR = Bk::TPR, RG = Bk::RG, RPL = Bk::RPL;
+  constexpr int NPAIR = RPL / 2;
+  __shared__ uint32_t ppair[2][NPAIR][RG][QG];  // [parity][pair][row group][query]
+
+  const int lane = threadIdx.x;
+  const int lq = lane & 31, lh = lane >> 5;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y / n_pass, q0 = (blockIdx.y % n_pass) * QG;
+  const int b = blockIdx.z;
+  const int nq = min(QG, a.NQ - q0);
+  const int c0 = split * a.chunk;
+  const int c1 = min(a.n_keys, c0 + a.chunk);
+  const int nblk = (c1 - c0 + 31) / 32;
+  int cur = 0;
+  if constexpr (DECODE) cur = a.cur_pos[b];
+
+  // Q^T (B operand): lane holds query lq, columns 16ks + 8lh .. +7
+  bf16x8 qf[KS];
+  {
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q);
+    long long row = -1;
+    if (lq < nq) {
+      if constexpr (DECODE) row = (long long)(q0 + lq) * a.q_sq;
+      else row = (long long)gl.idx[b * G + q0 + lq] * a.q_sq;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      U4 u = U4{{0, 0, 0, 0}};
+      if (row >= 0)
+        u = *reinterpret_cast<const U4 *>(qg + b * a.q_sb + kvh * a.q_sh + row + ks * 16 + lh * 8);
+      qf[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  const uint16_t *kbase = static_cast<const uint16_t *>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const uint16_t *vbase = static_cast<const uint16_t *>(a.v) + b * a.k_sb + kvh * a.k_sh;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[QG][8];
+#pragma unroll
+  for (int q = 0; q < QG; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+  const int g = lane / TPR;
+
+  DecBlock<D> blk;
+  if (nblk > 0) {
+    dec_load_k<D>(blk, kbase, a, c0, c1, lane);
+    dec_load_v<D>(blk, vbase, a, c0, c1, lane);
+    blk.valid = dec_valid<D, DECODE>(a, b, c0, c1, cur, lane);
+  }
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int parity = ib & 1;
+    const int s_next = c0 + 32 * (ib + 1);
+    const bool more = ib + 1 < nblk;
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, blk.k[ks]), qf[ks], s,
+                                                  0, 0, 0);
+    // accumulator element j holds key 8(j/4) + 4lh + (j%4) of the block
+    const unsigned long long vm = __ballot(lane < 32 && blk.valid);
+    // K registers are free again: start the next block's K (and mask) loads
+    if (more) {
+      dec_load_k<D>(blk, kbase, a, s_next, c1, lane);
+      blk.valid = dec_valid<D, DECODE>(a, b, s_next, c1, cur, lane);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = 8 * (j >> 2) + 4 * lh + (j & 3);
+      if (!((vm >> key) & 1ull)) s[j] = -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    mx = xhalf_max(mx);
+    const float m_new = fmaxf(m_run, mx * a.sl2);
+    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], a.sl2, -mu));
+      rs += s[j];
+    }
+    l_run = fmaf(l_run, alpha, xhalf_add(rs));
+    m_run = m_new;
+    // P pairs -> LDS.  Rows paired as (key, key + 8): both live in this lane
+    // as elements j and j + 4.
+    if (lq < QG) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if ((j & 4) == 0) {
+          int pi, rg;
+          if constexpr (D == 128) {  // row = 4i + rg, i = 2(j/4) + lh, pairs (i, i+2)
+            pi = (j >> 3) * 2 + lh;
+            rg = j & 3;
+          } else {                   // row = 8i + rg, i = j/4, pairs (i, i+1)
+            pi = j >> 3;
+            rg = 4 * lh + (j & 3);
+          }
+          ppair[parity][pi][rg][lq] = pack2_bf16(s[j], s[j + 4]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+      // alpha of query q lives in lane q
+      const float aq = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alpha), q));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] *= aq;
+    }
+#pragma unroll
+    for (int pi = 0; pi < NPAIR; ++pi) {
+      int i0, i1;
+      if constexpr (D == 128) {
+        i0 = (pi >> 1) * 4 + (pi & 1);
+        i1 = i0 + 2;
+      } else {
+        i0 = 2 * pi;
+        i1 = i0 + 1;
+      }
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x0 = blk.v[i0].w[e], x1 = blk.v[i1].w[e];
+        w[2 * e] = (x0 & 0xffffu) | (x1 << 16);
+        w[2 * e + 1] = (x0 >> 16) | (x1 & 0xffff0000u);
+      }
+#pragma unroll
+      for (int q = 0; q < QG; ++q) {
+        const uint32_t pp = ppair[parity][pi][g][q];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[q][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp),
+                                                      __builtin_bit_cast(bf16x2, w[e]), acc[q][e],
+                                                      false);
+      }
+    }
+    // V registers are free again: start the next block's V loads
+    if (more) dec_load_v<D>(blk, vbase, a, s_next, c1, lane);
+  }
+
+  // reduce acc over the row groups (lanes with equal lane % TPR)
+#pragma unroll
+  for (int q = 0; q < QG; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[q][e];
+#pragma unroll
+      for (int sft = TPR; sft < 64; sft <<= 1) x += __shfl_xor(x, sft);
+      acc[q][e] = x;
+    }
+  const long long base = ((long long)b * a.NKV + kvh) * a.NQ;
+  if (lane < TPR) {
+#pragma unroll
+    for (int q = 0; q < QG; ++q) {
+      if (q < nq) {
+        float *dst = a.ws + ((base + q0 + q) * a.S + split) * (D + 2) + lane * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = acc[q][e];
+      }
+    }
+  }
+  if (lh == 0 && lq < nq) {
+    float *dst = a.ws + ((base + q0 + lq) * a.S + split) * (D + 2);
+    dst[D] = m_run;
+    dst[D + 1] = l_run;
+  }
+}
+
+template <int D, bool DECODE>
+hipError_t run_mfma(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) {
+  const int nq = a.NQ;
+  const int qg = nq >= 8 ? 8 : nq >= 4 ? 4 : nq >= 2 ? 2 : 1;
+  const int n_pass = (nq + qg - 1) / qg;
+  dim3 grid(a.S, a.NKV * n_pass, a.B);
+  switch (qg) {
+    case 8: hipLaunchKernelGGL((split_mfma_kernel<D, 8, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
+    case 4: hipLaunchKernelGGL((split_mfma_kernel<D, 4, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
+    case 2: hipLaunchKernelGGL((split_mfma_kernel<D, 2, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
+    default: hipLaunchKernelGGL((split_mfma_kernel<D, 1, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
+  }
+  hipLaunchKernelGGL((combine_kernel<D, false, DECODE>), dim3(a.NQ, a.NKV, a.B), dim3(D), 0, st, a,
+                     *gl, G);
+  return hipGetLastError();
+}
+
 template <int D, bool F32, bool DECODE>
 hipError_t run(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) {
   dim3 grid(a.S, a.NKV, a.B);
@@ -275,10 +552,10 @@ hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const 
   (void)H;
   if (decode) {
     if (f32) return D == 128 ? run<128, true, true>(a, gl, G, st) : run<64, true, true>(a, gl, G, st);
-    return D == 128 ? run<128, false, true>(a, gl, G, st) : run<64, false, true>(a, gl, G, st);
+    return D == 128 ? run_mfma<128, true>(a, gl, G, st) : run_mfma<64, true>(a, gl, G, st);
   }
   if (f32) return D == 128 ? run<128, true, false>(a, gl, G, st) : run<64, true, false>(a, gl, G, st);
-  return D == 128 ? run<128, false, false>(a, gl, G, st) : run<64, false, false>(a, gl, G, st);
+  return D == 128 ? run_mfma<128, false>(a, gl, G, st) : run_mfma<64, false>(a, gl, G, st);
 }
 
 int split_max_chunk() { return kMaxChunk; }

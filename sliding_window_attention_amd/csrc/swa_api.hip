@@ -35,8 +35,15 @@ int choose_splits(long long heads_total, int n_keys) {
   long long want = (2048 + heads_total - 1) / heads_total;
   int s = (int)std::max<long long>(s_min, std::min<long long>(want, s_max));
   if (s < 1) s = 1;
-  const int chunk = (n_keys + s - 1) / s;
+  int chunk = (n_keys + s - 1) / s;
+  chunk = std::min(maxc, (chunk + 31) / 32 * 32);  // whole 32-key blocks
   return (n_keys + chunk - 1) / chunk;
+}
+
+// Keys per split for S splits (whole 32-key blocks, at most the kernel maximum).
+int split_chunk(int n_keys, int S) {
+  int chunk = (n_keys + S - 1) / S;
+  return std::min(split_max_chunk(), (chunk + 31) / 32 * 32);
 }
 
 swa_status hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
@@ -163,7 +170,7 @@ swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const vo
   a.B = B; a.NKV = H_kv; a.NQ = H_q / H_kv;
   a.n_keys = W;
   a.S = choose_splits((long long)B * H_kv, W);
-  a.chunk = (W + a.S - 1) / a.S;
+  a.chunk = split_chunk(W, a.S);
   a.W = W;
   a.q_sq = d_h; a.q_sh = (long long)a.NQ * d_h; a.q_sb = (long long)H_q * d_h;
   a.o_sq = a.q_sq; a.o_sh = a.q_sh; a.o_sb = a.q_sb;
@@ -261,7 +268,7 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   s.B = B; s.NKV = H; s.NQ = G;
   s.n_keys = T;
   s.S = choose_splits((long long)B * H, T);
-  s.chunk = (T + s.S - 1) / s.S;
+  s.chunk = split_chunk(T, s.S);
   s.q_sb = a.q_sb; s.q_sh = d_h; s.q_sq = a.q_st;
   s.o_sb = a.q_sb; s.o_sh = d_h; s.o_sq = a.q_st;
   s.k_sb = a.k_sb; s.k_sh = d_h; s.k_sr = a.k_st;
