@@ -10,8 +10,13 @@
 //   online softmax   each lane owns one query row: the row max / sum over the
 //                    32x32 accumulator is a 16-register reduction plus one
 //                    v_permlane32_swap with the partner half-wave
-//   O^T += V^T P^T   P^T stays in VGPRs as the B operand; V^T comes from LDS,
-//                    transposed while staging the tile
+//   O^T += V^T P^T   P^T stays in VGPRs as the B operand; the V^T operand is
+//                    read from the row-major V tile with ds_read_b64_tr_b16
+//
+// K and V tiles go from HBM to LDS with global_load_lds_dwordx4 (no VGPR
+// staging), double-buffered: tile j+1 is in flight while tile j is computed.
+// Each 16-byte chunk of a tile row is XOR-swizzled by the row index so both the
+// K operand reads and the transposing V reads hit distinct LDS banks.
 //
 // The score definition is the masked softmax of [KB] §2 (alpha^SWA, o^SWA);
 // windows: causal t-W < s <= t ([KB] §2-§3), or, in symmetric mode, the
@@ -57,95 +62,61 @@ __device__ inline float xhalf_add(float x) {
 }
 
 // ---- LDS layouts ---------------------------------------------------------------
-// K tile: [64 keys][D] bf16; the 16-byte chunk c of key row s sits at chunk
-// c ^ (s & 7), so the 8 lanes of an MFMA operand read (8 rows, same chunk)
-// touch 8 distinct bank groups.
+#define AS1 __attribute__((address_space(1)))
+#define AS3 __attribute__((address_space(3)))
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
-__device__ inline int k_off(int key, int chunk) {
-  return key * D + ((chunk ^ (key & 7)) << 3);
-}
-// V^T tile: [D][64 key positions] bf16.  Keys are permuted inside each group
-// of 16 (bits 2 and 3 swapped) so that the 8 keys one lane feeds to the PV
-// MFMA are contiguous, and chunks are XOR-swizzled by (d ^ d>>3) & 7 so both
-// the operand reads (consecutive d) and the staging writes (d spaced by 8)
-// spread over the banks.
-__device__ inline int vpos(int key) {
-  return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-__device__ inline int vt_off(int d, int pos) {
-  return d * kBN + ((((pos >> 3) ^ ((d ^ (d >> 3)) & 7))) << 3) + (pos & 7);
-}
+struct Geo {
+  static constexpr int ROWB = 2 * D;           // bytes per K/V row
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;      // rows per DMA wave-instruction (4 or 8)
+  static constexpr int NI = kBN / RPI;         // DMA instructions per tile and tensor
+  static constexpr int NIW = NI / kWaves;      // ... per wave
+  static constexpr int TILE_B = kBN * ROWB;    // bytes per K (or V) tile
+};
+
+// Physical chunk = logical chunk ^ swz(row).
+// K: the 16 lanes serviced together read 16 consecutive rows at one logical
+//    chunk; swz_k gives them 16 distinct 16-byte bank groups.
+// V: a transposing read touches 4 consecutive rows x 4 chunks per half-wave;
+//    swz_v spreads those 16 chunks over all bank groups.
+template <int D>
+__device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ inline int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 template <int D>
 struct Smem {
-  static constexpr int kTile = kBN * D;           // elements per K (or V^T) tile
-  uint16_t kv[2][2][kTile];                        // [buffer][K, V^T]
+  char buf[2][2][Geo<D>::TILE_B];  // [stage][K, V], row-major tiles, swizzled chunks
 };
 
-// ---- per-tile staging ------------------------------------------------------------
-// Thread t loads KPT consecutive key rows x 8 columns (16 bytes each), so the
-// V^T store can pack KPT keys per column.  Rows of one wave-instruction are
-// full contiguous d_h-wide rows (coalesced).
-template <int D>
-struct Stage {
-  static constexpr int TPR = D / 8;          // threads per row
-  static constexpr int KPT = kBN * TPR / 256; // keys per thread (4 for D=128, 2 for D=64)
-  U4 k[KPT], v[KPT];
-};
-
-template <int D>
-__device__ inline void stage_load(Stage<D> &st, const uint16_t *kbase, const uint16_t *vbase,
-                                  const long long *row_off, int tid) {
-  constexpr int TPR = Stage<D>::TPR, KPT = Stage<D>::KPT;
-  const int chunk = tid % TPR;
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const long long off = row_off[r];
-    if (off >= 0) {
-      st.k[r] = *reinterpret_cast<const U4 *>(kbase + off + chunk * 8);
-      st.v[r] = *reinterpret_cast<const U4 *>(vbase + off + chunk * 8);
-    } else {
-      st.k[r] = U4{{0, 0, 0, 0}};
-      st.v[r] = U4{{0, 0, 0, 0}};
-    }
-  }
+__device__ inline void dma16(const char *g, char *l) {
+  __builtin_amdgcn_global_load_lds((const AS1 void *)g, (AS3 void *)l, 16, 0, 0);
 }
 
-template <int D>
-__device__ inline void stage_store(const Stage<D> &st, uint16_t *ks, uint16_t *vts, int tid) {
-  constexpr int TPR = Stage<D>::TPR, KPT = Stage<D>::KPT;
-  const int chunk = tid % TPR;
-  const int key0 = KPT * (tid / TPR);
-#pragma unroll
-  for (int r = 0; r < KPT; ++r)
-    *reinterpret_cast<U4 *>(ks + k_off<D>(key0 + r, chunk)) = st.k[r];
-  const int p = vpos(key0);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = chunk * 8 + e;
-    const int word = e >> 1, hi = e & 1;
-    uint32_t h[KPT];
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) h[r] = hi ? (st.v[r].w[word] >> 16) : (st.v[r].w[word] & 0xffffu);
-    if constexpr (KPT == 4) {
-      uint2 out;
-      out.x = h[0] | (h[1] << 16);
-      out.y = h[2] | (h[3] << 16);
-      *reinterpret_cast<uint2 *>(vts + vt_off(d, p)) = out;
-    } else {
-      *reinterpret_cast<uint32_t *>(vts + vt_off(d, p)) = h[0] | (h[1] << 16);
-    }
-  }
+__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)p0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)p1);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
 }
 
 // ---- the kernel ------------------------------------------------------------------
+
+// Largest growth (log2 units) of a row max tolerated before the running
+// reference max is raised and O, l are rescaled.
+constexpr float kLazy = 8.f;
 
 template <int D, bool SYM>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const GlobalList gl) {
   __shared__ Smem<D> sm;
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
-  constexpr int KPT = Stage<D>::KPT, TPR = Stage<D>::TPR;
+  using Gm = Geo<D>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -220,23 +191,79 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   const int n_glob = SYM ? ceil_div(a.G, kBN) : 0;
   const int n_tiles = n_win + n_glob;
 
-  // rows this thread stages for tile j (element offsets from kbase; -1 = zero fill)
-  auto rows_for = [&](int j, long long *off) {
-    const int key0 = KPT * (tid / TPR);
-    if (j < n_win) {
-      const int s0 = (tr.lo + j) * kBN + key0;
+  // -------- DMA addressing.  Wave instruction i of a tile covers rows
+  // i*RPI .. i*RPI+RPI-1; lane l lands at LDS byte 16*l of that 1 KB, i.e. row
+  // i*RPI + l/CPR, physical chunk l%CPR, so it loads logical chunk
+  // (l%CPR) ^ swz(row).  Rows of a window tile are consecutive class rows, so
+  // the per-lane byte offsets are fixed and each tile adds a uniform base.
+  const long long rs_b = k_rowstride * 2;  // bytes between consecutive class rows
+  uint32_t koff[Gm::NIW], voff[Gm::NIW];
+  int dma_row[Gm::NIW], dma_ck[Gm::NIW], dma_cv[Gm::NIW];
 #pragma unroll
-      for (int r = 0; r < KPT; ++r)
-        off[r] = (s0 + r < n_cls) ? k_rho + (long long)(s0 + r) * k_rowstride : -1;
+  for (int t = 0; t < Gm::NIW; ++t) {
+    const int r = (wave * Gm::NIW + t) * Gm::RPI + lane / Gm::CPR;
+    const int p = lane % Gm::CPR;
+    dma_row[t] = r;
+    dma_ck[t] = (p ^ swz_k<D>(r)) * 16;
+    dma_cv[t] = (p ^ swz_v<D>(r)) * 16;
+    koff[t] = (uint32_t)(r * rs_b) + dma_ck[t];
+    voff[t] = (uint32_t)(r * rs_b) + dma_cv[t];
+  }
+  const char *kb8 = reinterpret_cast<const char *>(kbase);
+  const char *vb8 = reinterpret_cast<const char *>(vbase);
+  auto issue = [&](int j, int stage) {
+    char *lk = sm.buf[stage][0] + wave * Gm::NIW * 1024;
+    char *lv = sm.buf[stage][1] + wave * Gm::NIW * 1024;
+    if (j < n_win && (tr.lo + j) * kBN + kBN <= n_cls) {
+      // whole tile inside the class: uniform base + fixed lane offsets
+      const long long base = (k_rho + (long long)(tr.lo + j) * kBN * k_rowstride) * 2;
+#pragma unroll
+      for (int t = 0; t < Gm::NIW; ++t) {
+        dma16(kb8 + base + koff[t], lk + t * 1024);
+        dma16(vb8 + base + voff[t], lv + t * 1024);
+      }
     } else {
-      const int u0 = (j - n_win) * kBN + key0;
+      // ragged last tile (rows clamped to the last valid row; the mask
+      // removes them) or a tile of global keys (absolute positions)
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        // global keys are absolute positions
-        off[r] = (u0 + r < a.G) ? (long long)gl.idx[b * a.G + u0 + r] * a.k_st : -1;
+      for (int t = 0; t < Gm::NIW; ++t) {
+        long long off;
+        if (j < n_win) {
+          const int sr = min((tr.lo + j) * kBN + dma_row[t], n_cls - 1);
+          off = (k_rho + (long long)sr * k_rowstride) * 2;
+        } else {
+          const int u = min((j - n_win) * kBN + dma_row[t], a.G - 1);
+          off = (long long)gl.idx[b * a.G + u] * a.k_st * 2;
+        }
+        dma16(kb8 + off + dma_ck[t], lk + t * 1024);
+        dma16(vb8 + off + dma_cv[t], lv + t * 1024);
       }
     }
   };
+
+  // -------- operand read offsets (bytes within a tile)
+  // K (A operand of S^T): lane reads row 32kb + lq, logical chunk 2kk + lh.
+  uint32_t kop[KS_QK];
+#pragma unroll
+  for (int kk = 0; kk < KS_QK; ++kk)
+    kop[kk] = lq * Gm::ROWB + (((2 * kk + lh) ^ swz_k<D>(lq)) * 16);
+  // V^T (A operand of O^T): two transposing reads per 16-key step.  In each
+  // group of 16 lanes, source lane s addresses row 16kk + 4hh + s/4 at columns
+  // 32db + 16dg + 4(s%4) .. +3, so output lane i of the group receives column
+  // 32db + 16dg + i of those 4 rows; the second read adds 8 rows.  The 8 keys
+  // a lane gets are 16kk + {4hh..4hh+3, 8+4hh..8+4hh+3}, the order in which
+  // the P^T B operand holds them.
+  uint32_t vop[DB];
+  {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int hh = grp >> 1, dg = grp & 1;
+    const int row = 4 * hh + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * dg + ((sl >> 1) & 1);
+      vop[db] = row * Gm::ROWB + ((c ^ swz_v<D>(row)) * 16) + 8 * (sl & 1);
+    }
+  }
 
   // -------- running softmax state (lane owns query row lq; both half-waves agree)
   f32x16 acc_o[DB];
@@ -245,35 +272,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   float m_run = -INFINITY, l_run = 0.f;
   const int my_row = row0 + lq;
 
-  Stage<D> st;
-  {
-    long long off[KPT];
-    rows_for(0, off);
-    stage_load<D>(st, kbase, vbase, off, tid);
-    stage_store<D>(st, sm.kv[0][0], sm.kv[0][1], tid);
-  }
+  issue(0, 0);
+  wait_dma();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) {
-      long long off[KPT];
-      rows_for(j + 1, off);
-      stage_load<D>(st, kbase, vbase, off, tid);
-    }
-    const uint16_t *ks = sm.kv[buf][0];
-    const uint16_t *vts = sm.kv[buf][1];
+    if (j + 1 < n_tiles) issue(j + 1, buf ^ 1);
+    const char *ks = sm.buf[buf][0];
+    const char *vs = sm.buf[buf][1];
 
     // ---- S^T = K Q^T : two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const int key = kb * 32 + lq;
 #pragma unroll
       for (int kk = 0; kk < KS_QK; ++kk) {
-        const U4 u = *reinterpret_cast<const U4 *>(ks + k_off<D>(key, 2 * kk + lh));
+        const U4 u = *reinterpret_cast<const U4 *>(ks + kb * 32 * Gm::ROWB + kop[kk]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), qf[kk], s[kb], 0, 0, 0);
       }
     }
@@ -314,16 +330,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
         }
     }
 
-    // ---- online softmax in the log2 domain (sl2 = scale * log2 e)
-    float mx = s[0][0];
+    // ---- online softmax in the log2 domain (sl2 = scale * log2 e).  The
+    // reference max m_run is only raised when some row of the wave would
+    // otherwise see p = 2^(s - m_run) above 2^kLazy; l and O share the same
+    // reference, so the result is unchanged and O is rarely rescaled.
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[0][e]);
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[0][e], s[0][e + 1]));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[1][e]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx * a.sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[1][e], s[1][e + 1]));
+    mx = xhalf_max(mx) * a.sl2;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) acc_o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -333,11 +358,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
         s[kb][e] = p;
         rs += p;
       }
-    rs = xhalf_add(rs);
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) acc_o[i] *= alpha;
+    l_run += xhalf_add(rs);
 
     // ---- O^T += V^T P^T : 4 key steps of 16
 #pragma unroll
@@ -351,19 +372,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
       const bf16x8 pb = as_bf16x8(pu);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const U4 u = *reinterpret_cast<const U4 *>(vts + vt_off(db * 32 + lq, kk * 16 + lh * 8));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), pb, acc_o[db], 0, 0, 0);
+        const char *p0 = vs + kk * 16 * Gm::ROWB + vop[db];
+        const bf16x8 vt = tr_read8(p0, p0 + 8 * Gm::ROWB);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pb, acc_o[db], 0, 0, 0);
       }
     }
 
-    if (has_next) stage_store<D>(st, sm.kv[buf ^ 1][0], sm.kv[buf ^ 1][1], tid);
+    wait_dma();
     __syncthreads();
   }
 
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
   const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
   constexpr int OP = D + 8;  // staging pitch (elements)
-  uint16_t *ost = &sm.kv[0][0][0] + wave * (kRowsPerWave * OP);
+  uint16_t *ost = reinterpret_cast<uint16_t *>(&sm.buf[0][0][0]) + wave * (kRowsPerWave * OP);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll

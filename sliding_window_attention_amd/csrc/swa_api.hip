@@ -136,7 +136,9 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
   std::memset(&gl, 0, sizeof(gl));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, false, d_h, &gl, st));
-  if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL) return SWA_ERR_UNSUPPORTED;
+  // bf16 kernels address one batch slice of K/V with 32-bit byte offsets
+  if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31))
+    return SWA_ERR_UNSUPPORTED;
   return hip_status(launch_fwd_bf16(a, false, d_h, &gl, st));
 }
 
@@ -249,7 +251,8 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
     tiles += class_tiles(T, d, a.BM);
   }
   a.head_off[H] = (int)tiles;
-  if (tiles * B > 0x7fffffffLL) return SWA_ERR_UNSUPPORTED;
+  if (tiles * B > 0x7fffffffLL || (dt == SWA_BF16 && a.k_sb * 2 >= (1LL << 31)))
+    return SWA_ERR_UNSUPPORTED;
   a.tiles_per_batch = (int)tiles;
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
