@@ -35,6 +35,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct alignas(16) U4 {
   uint32_t w[4];
@@ -44,7 +45,6 @@ __device__ inline bf16x8 as_bf16x8(U4 u) { return __builtin_bit_cast(bf16x8, u);
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
   // v_cvt_pk_bf16_f32: round-to-nearest-even on both halves
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 v;
   v[0] = (__bf16)a;
   v[1] = (__bf16)b;
@@ -86,15 +86,61 @@ __device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1
 template <int D>
 __device__ inline int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-template <int D>
-struct Smem {
-  char buf[2][2][Geo<D>::TILE_B];  // [stage][K, V], row-major tiles, swizzled chunks
-};
 
-__device__ inline void dma16(const char *g, char *l) {
-  __builtin_amdgcn_global_load_lds((const AS1 void *)g, (AS3 void *)l, 16, 0, 0);
+__device__ inline uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t)(AS3 const char *)p; }
+
+// Values the compiler cannot prove wave-uniform (they derive from blockIdx and
+// the wave index) are pinned to scalar registers.
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline const char *uni_ptr(const char *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char *)(((uint64_t)hi << 32) | lo);
 }
 
+// HBM -> LDS copies with global_load_lds_dwordx4: lane i's 16 bytes land at
+// LDS byte m0 + 16*i.  One call issues a wave's N copies of a tile (1 KB each,
+// consecutive in LDS), global address = scalar base + per-lane 32-bit offset.
+// Issued from inline assembly so the compiler does not track them: it would
+// otherwise wait for every outstanding copy before any LDS read, even of the
+// other stage.  The kernel waits (s_waitcnt vmcnt(0)) and barriers before a
+// freshly loaded stage is read.  m0 (a reserved register) is restored.
+template <int N>
+__device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t lds) {
+  uint32_t saved;
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %3, %2\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %4, %2\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %5, %2\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %6, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3])
+        : "scc");
+  } else {
+    static_assert(N == 2, "2 or 4 copies per wave and tile");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %3, %2\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "global_load_lds_dwordx4 %4, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1])
+        : "scc");
+  }
+}
+
+// Drain this wave's copies.  Inline assembly: the compiler does not know about
+// the copies and would drop a wait it considers redundant.
 __device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
@@ -113,13 +159,20 @@ constexpr float kLazy = 8.f;
 
 template <int D, bool SYM>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const GlobalList gl) {
-  __shared__ Smem<D> sm;
+  // Row-major K and V tiles (swizzled chunks), two stages each.  Separate
+  // arrays let the compiler see that a DMA into one stage never aliases the
+  // operand reads of the other, so no wait is placed in front of those reads.
+  __shared__ __attribute__((aligned(1024))) char lk0[Geo<D>::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char lk1[Geo<D>::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char lv0[Geo<D>::TILE_B];
+  __shared__ __attribute__((aligned(1024))) char lv1[Geo<D>::TILE_B];
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
   using Gm = Geo<D>;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lq = lane & 31, lh = lane >> 5;
 
   // -------- work decode
@@ -157,6 +210,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
     tile_row0 = tile * a.BM;
     row0 = tile_row0 + wave * kRowsPerWave;
   }
+  b = uni(b);
+  h = uni(h);
+  kvh = uni(kvh);
+  rho = uni(rho);
+  dil = uni(dil);
+  n_cls = uni(n_cls);
+  tile_row0 = uni(tile_row0);
+  row0 = uni(row0);
   const int t1_valid = min(tile_row0 + a.BM, n_cls) - 1;  // last valid row of the tile
 
   const uint16_t *qg = static_cast<const uint16_t *>(a.q);
@@ -181,12 +242,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
       if (r < n_cls) u = *reinterpret_cast<const U4 *>(qp + ks * 16 + lh * 8);
       qf[ks] = as_bf16x8(u);
     }
+    // Make the compiler wait for the Q loads here, before the tile loop: the
+    // copies issued in the loop are invisible to its counter tracking, so a
+    // wait for Q placed inside the loop would also stall on them.
+#pragma unroll
+    for (int ks = 0; ks < KS_QK; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   // -------- schedule
   TileRange tr;
   if constexpr (!SYM) tr = causal_tile_range(tile_row0, t1_valid, a.W, kBN);
   else tr = sym_tile_range(tile_row0, t1_valid, a.W, n_cls, kBN);
+  tr.lo = uni(tr.lo);
+  tr.hi = uni(tr.hi);
   const int n_win = tr.hi - tr.lo + 1;
   const int n_glob = SYM ? ceil_div(a.G, kBN) : 0;
   const int n_tiles = n_win + n_glob;
@@ -198,46 +266,45 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   // the per-lane byte offsets are fixed and each tile adds a uniform base.
   const long long rs_b = k_rowstride * 2;  // bytes between consecutive class rows
   uint32_t koff[Gm::NIW], voff[Gm::NIW];
-  int dma_row[Gm::NIW], dma_ck[Gm::NIW], dma_cv[Gm::NIW];
 #pragma unroll
   for (int t = 0; t < Gm::NIW; ++t) {
     const int r = (wave * Gm::NIW + t) * Gm::RPI + lane / Gm::CPR;
     const int p = lane % Gm::CPR;
-    dma_row[t] = r;
-    dma_ck[t] = (p ^ swz_k<D>(r)) * 16;
-    dma_cv[t] = (p ^ swz_v<D>(r)) * 16;
-    koff[t] = (uint32_t)(r * rs_b) + dma_ck[t];
-    voff[t] = (uint32_t)(r * rs_b) + dma_cv[t];
+    koff[t] = (uint32_t)(r * rs_b) + (p ^ swz_k<D>(r)) * 16;
+    voff[t] = (uint32_t)(r * rs_b) + (p ^ swz_v<D>(r)) * 16;
   }
   const char *kb8 = reinterpret_cast<const char *>(kbase);
   const char *vb8 = reinterpret_cast<const char *>(vbase);
-  auto issue = [&](int j, int stage) {
-    char *lk = sm.buf[stage][0] + wave * Gm::NIW * 1024;
-    char *lv = sm.buf[stage][1] + wave * Gm::NIW * 1024;
+  // DMA of the K (which = 0) or V (which = 1) rows of tile j (window tiles
+  // j < n_win, then tiles of global keys) into the LDS tile at `dst`.
+  auto issue = [&](int j, uint32_t dst, int which) {
+    const uint32_t ld = dst + wave * Gm::NIW * 1024;
+    const char *g8 = which ? vb8 : kb8;
+    uint32_t off[Gm::NIW];
     if (j < n_win && (tr.lo + j) * kBN + kBN <= n_cls) {
       // whole tile inside the class: uniform base + fixed lane offsets
       const long long base = (k_rho + (long long)(tr.lo + j) * kBN * k_rowstride) * 2;
 #pragma unroll
-      for (int t = 0; t < Gm::NIW; ++t) {
-        dma16(kb8 + base + koff[t], lk + t * 1024);
-        dma16(vb8 + base + voff[t], lv + t * 1024);
-      }
+      for (int t = 0; t < Gm::NIW; ++t) off[t] = which ? voff[t] : koff[t];
+      dma_tile<Gm::NIW>(g8 + base, off, ld);
     } else {
       // ragged last tile (rows clamped to the last valid row; the mask
       // removes them) or a tile of global keys (absolute positions)
 #pragma unroll
       for (int t = 0; t < Gm::NIW; ++t) {
-        long long off;
+        const int r = (wave * Gm::NIW + t) * Gm::RPI + lane / Gm::CPR;
+        const int p = lane % Gm::CPR;
+        long long o;
         if (j < n_win) {
-          const int sr = min((tr.lo + j) * kBN + dma_row[t], n_cls - 1);
-          off = (k_rho + (long long)sr * k_rowstride) * 2;
+          const int sr = min((tr.lo + j) * kBN + r, n_cls - 1);
+          o = (k_rho + (long long)sr * k_rowstride) * 2;
         } else {
-          const int u = min((j - n_win) * kBN + dma_row[t], a.G - 1);
-          off = (long long)gl.idx[b * a.G + u] * a.k_st * 2;
+          const int u = min((j - n_win) * kBN + r, a.G - 1);
+          o = (long long)gl.idx[b * a.G + u] * a.k_st * 2;
         }
-        dma16(kb8 + off + dma_ck[t], lk + t * 1024);
-        dma16(vb8 + off + dma_cv[t], lv + t * 1024);
+        off[t] = (uint32_t)o + (which ? (p ^ swz_v<D>(r)) : (p ^ swz_k<D>(r))) * 16;
       }
+      dma_tile<Gm::NIW>(g8, off, ld);
     }
   };
 
@@ -272,74 +339,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   float m_run = -INFINITY, l_run = 0.f;
   const int my_row = row0 + lq;
 
-  issue(0, 0);
-  wait_dma();
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) issue(j + 1, buf ^ 1);
-    const char *ks = sm.buf[buf][0];
-    const char *vs = sm.buf[buf][1];
-
-    // ---- S^T = K Q^T : two 32-key blocks
-    f32x16 s[2];
+  // ---- building blocks.  Accumulator element (kb, e) of S^T holds key
+  // 32kb + 8(e/4) + 4lh + (e%4) of the tile, for query row my_row.
+  auto qk = [&](const char *ks, f32x16 *sv) {
+    sv[0] = f32x16{};
+    sv[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    for (int kk = 0; kk < KS_QK; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < KS_QK; ++kk) {
+      for (int kb = 0; kb < 2; ++kb) {
         const U4 u = *reinterpret_cast<const U4 *>(ks + kb * 32 * Gm::ROWB + kop[kk]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), qf[kk], s[kb], 0, 0, 0);
+        sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), qf[kk], sv[kb], 0, 0, 0);
       }
-    }
-
-    // ---- mask (partial tiles only).  Accumulator element (kb, e) holds key
-    // 32kb + 8(e/4) + 4lh + (e%4) of the tile, for query row my_row.
-    bool full;
-    int key_base;
-    if (j < n_win) {
-      const int kj = tr.lo + j;
-      key_base = kj * kBN;
-      if constexpr (!SYM) full = causal_tile_full(tile_row0, t1_valid, kj, kBN, a.W, n_cls);
-      else full = sym_tile_full(tile_row0, t1_valid, kj, kBN, a.W, n_cls);
-    } else {
-      key_base = (j - n_win) * kBN;
-      full = false;
-    }
-    if (!full) {
+  };
+  // row max over the tile, in log2 units (sl2 = scale * log2 e)
+  auto rowmax = [&](const f32x16 *sv) {
+    float mx = fmaxf(sv[0][0], sv[0][1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[0][e], sv[0][e + 1]));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = key_base + kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          bool ok;
-          if (j < n_win) {
-            if constexpr (!SYM) ok = causal_in(my_row, kk, a.W) && kk < n_cls;
-            else ok = sym_in(my_row, kk, a.W) && kk < n_cls;
-          } else {
-            // global key u = kk: attended unless already inside this row's window
-            ok = false;
-            if (kk < a.G) {
-              const int g = gl.idx[b * a.G + kk];
-              const int i_abs = rho + dil * my_row;
-              ok = !dilated_in(i_abs, g, a.W, dil);
-            }
-          }
-          if (!ok) s[kb][e] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax in the log2 domain (sl2 = scale * log2 e).  The
-    // reference max m_run is only raised when some row of the wave would
-    // otherwise see p = 2^(s - m_run) above 2^kLazy; l and O share the same
-    // reference, so the result is unchanged and O is rarely rescaled.
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[0][e], s[0][e + 1]));
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[1][e], s[1][e + 1]));
-    mx = xhalf_max(mx) * a.sl2;
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[1][e], sv[1][e + 1]));
+    return xhalf_max(mx) * a.sl2;
+  };
+  // The reference max m_run is only raised when some row of the wave would
+  // otherwise see p = 2^(s - m_run) above 2^kLazy; l and O share the same
+  // reference, so the result is unchanged and O is rarely rescaled.
+  auto rescale = [&](float mx) {
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -348,28 +373,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
       for (int i = 0; i < DB; ++i) acc_o[i] *= alpha;
       m_run = m_new;
     }
+  };
+  // p = 2^(s*sl2 - m), row sum into l, P -> bf16 (RNE) packed as the B
+  // operands of the four PV k-steps
+  auto exp_pack = [&](f32x16 *sv, U4 *pu) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][e], a.sl2, -m_use));
-        s[kb][e] = p;
-        rs += p;
+        sv[kb][e] = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], a.sl2, -m_use));
+        rs += sv[kb][e];
       }
     l_run += xhalf_add(rs);
-
-    // ---- O^T += V^T P^T : 4 key steps of 16
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kb = kk >> 1, e0 = (kk & 1) * 8;
-      U4 pu;
-      pu.w[0] = pack_bf16(s[kb][e0 + 0], s[kb][e0 + 1]);
-      pu.w[1] = pack_bf16(s[kb][e0 + 2], s[kb][e0 + 3]);
-      pu.w[2] = pack_bf16(s[kb][e0 + 4], s[kb][e0 + 5]);
-      pu.w[3] = pack_bf16(s[kb][e0 + 6], s[kb][e0 + 7]);
-      const bf16x8 pb = as_bf16x8(pu);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pu[kk].w[w] = pack_bf16(sv[kb][e0 + 2 * w], sv[kb][e0 + 2 * w + 1]);
+    }
+  };
+  // O^T += V^T P^T : 4 key steps of 16
+  auto pv = [&](const char *vs, const U4 *pu) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 pb = as_bf16x8(pu[kk]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const char *p0 = vs + kk * 16 * Gm::ROWB + vop[db];
@@ -377,7 +406,59 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pb, acc_o[db], 0, 0, 0);
       }
     }
+  };
+  auto tile_full = [&](int j) {
+    if (j >= n_win) return false;  // tiles of global keys are always masked
+    const int kj = tr.lo + j;
+    if constexpr (!SYM) return causal_tile_full(tile_row0, t1_valid, kj, kBN, a.W, n_cls);
+    else return sym_tile_full(tile_row0, t1_valid, kj, kBN, a.W, n_cls);
+  };
+  // mask of a partial tile: window predicate, or for a tile of global keys
+  // the globals not already inside this row's (dilated) window
+  auto mask = [&](int j, f32x16 *sv) {
+    const int key_base = (j < n_win) ? (tr.lo + j) * kBN : (j - n_win) * kBN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = key_base + kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        bool ok;
+        if (j < n_win) {
+          if constexpr (!SYM) ok = causal_in(my_row, kk, a.W) && kk < n_cls;
+          else ok = sym_in(my_row, kk, a.W) && kk < n_cls;
+        } else {
+          ok = false;
+          if (kk < a.G) {
+            const int g = gl.idx[b * a.G + kk];
+            const int i_abs = rho + dil * my_row;
+            ok = !dilated_in(i_abs, g, a.W, dil);
+          }
+        }
+        if (!ok) sv[kb][e] = -INFINITY;
+      }
+  };
 
+  // ---- main loop: tile j+1 is copied into the other stage while tile j is
+  // computed; one barrier per tile.
+  const uint32_t a_k0 = lds_addr(lk0), a_k1 = lds_addr(lk1);
+  const uint32_t a_v0 = lds_addr(lv0), a_v1 = lds_addr(lv1);
+  issue(0, a_k0, 0);
+  issue(0, a_v0, 1);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    const int st = j & 1;
+    if (j + 1 < n_tiles) {
+      issue(j + 1, st ? a_k0 : a_k1, 0);
+      issue(j + 1, st ? a_v0 : a_v1, 1);
+    }
+    f32x16 sv[2];
+    U4 pu[4];
+    qk(st ? lk1 : lk0, sv);
+    if (!tile_full(j)) mask(j, sv);
+    rescale(rowmax(sv));
+    exp_pack(sv, pu);
+    pv(st ? lv1 : lv0, pu);
     wait_dma();
     __syncthreads();
   }
@@ -385,7 +466,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
   const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
   constexpr int OP = D + 8;  // staging pitch (elements)
-  uint16_t *ost = reinterpret_cast<uint16_t *>(&sm.buf[0][0][0]) + wave * (kRowsPerWave * OP);
+  // each wave stages its 32 rows in one of the four (now idle) tile buffers
+  static_assert(kRowsPerWave * OP * 2 <= Geo<D>::TILE_B, "O staging must fit a tile buffer");
+  char *stage_buf = wave == 0 ? lk0 : wave == 1 ? lk1 : wave == 2 ? lv0 : lv1;
+  uint16_t *ost = reinterpret_cast<uint16_t *>(stage_buf);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
