@@ -124,8 +124,16 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
         : "=&s"(saved)
         : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3])
         : "scc");
+  } else if constexpr (N == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %3, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]));
   } else {
-    static_assert(N == 2, "2 or 4 copies per wave and tile");
+    static_assert(N == 2, "1, 2 or 4 copies per wave and tile");
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
@@ -158,7 +166,7 @@ __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
 constexpr float kLazy = 8.f;
 
 template <int D, bool SYM>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const GlobalList gl) {
+__global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const GlobalList gl) {
   // Row-major K and V tiles (swizzled chunks), two stages each.  Separate
   // arrays let the compiler see that a DMA into one stage never aliases the
   // operand reads of the other, so no wait is placed in front of those reads.
@@ -168,6 +176,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   __shared__ __attribute__((aligned(1024))) char lv1[Geo<D>::TILE_B];
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
+  constexpr int KB = kBN / 32;   // 32-key blocks of S^T per tile
+  constexpr int PK = kBN / 16;   // 16-key k-steps of the PV product per tile
   using Gm = Geo<D>;
 
   const int tid = threadIdx.x;
@@ -342,12 +352,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   // ---- building blocks.  Accumulator element (kb, e) of S^T holds key
   // 32kb + 8(e/4) + 4lh + (e%4) of the tile, for query row my_row.
   auto qk = [&](const char *ks, f32x16 *sv) {
-    sv[0] = f32x16{};
-    sv[1] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sv[kb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KS_QK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const U4 u = *reinterpret_cast<const U4 *>(ks + kb * 32 * Gm::ROWB + kop[kk]);
         sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), qf[kk], sv[kb], 0, 0, 0);
       }
@@ -358,7 +368,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
 #pragma unroll
     for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[0][e], sv[0][e + 1]));
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[1][e], sv[1][e + 1]));
+    for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[kb][e], sv[kb][e + 1]));
     return xhalf_max(mx) * a.sl2;
   };
   // The reference max m_run is only raised when some row of the wave would
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         sv[kb][e] = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], a.sl2, -m_use));
@@ -388,16 +400,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
       }
     l_run += xhalf_add(rs);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < PK; ++kk) {
       const int kb = kk >> 1, e0 = (kk & 1) * 8;
 #pragma unroll
       for (int w = 0; w < 4; ++w) pu[kk].w[w] = pack_bf16(sv[kb][e0 + 2 * w], sv[kb][e0 + 2 * w + 1]);
     }
   };
-  // O^T += V^T P^T : 4 key steps of 16
+  // O^T += V^T P^T : key steps of 16
   auto pv = [&](const char *vs, const U4 *pu) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < PK; ++kk) {
       const bf16x8 pb = as_bf16x8(pu[kk]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -418,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
   auto mask = [&](int j, f32x16 *sv) {
     const int key_base = (j < n_win) ? (tr.lo + j) * kBN : (j - n_win) * kBN;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int kk = key_base + kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
@@ -452,8 +464,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
       issue(j + 1, st ? a_k0 : a_k1, 0);
       issue(j + 1, st ? a_v0 : a_v1, 1);
     }
-    f32x16 sv[2];
-    U4 pu[4];
+    f32x16 sv[KB];
+    U4 pu[PK];
     qk(st ? lk1 : lk0, sv);
     if (!tile_full(j)) mask(j, sv);
     rescale(rowmax(sv));
@@ -465,11 +477,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
 
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
   const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
-  constexpr int OP = D + 8;  // staging pitch (elements)
-  // each wave stages its 32 rows in one of the four (now idle) tile buffers
-  static_assert(kRowsPerWave * OP * 2 <= Geo<D>::TILE_B, "O staging must fit a tile buffer");
+  // Each wave stages its 32 rows (row-major, 16-byte chunks XOR-swizzled by
+  // row, no padding) in one of the four idle tile buffers.
+  static_assert(kRowsPerWave * D * 2 <= Geo<D>::TILE_B, "O staging must fit a tile buffer");
   char *stage_buf = wave == 0 ? lk0 : wave == 1 ? lk1 : wave == 2 ? lv0 : lv1;
   uint16_t *ost = reinterpret_cast<uint16_t *>(stage_buf);
+  constexpr int CPRo = D / 8;  // 16-byte chunks per staged row
+  auto ost_off = [&](int row, int col) {  // element offset of (row, col)
+    return row * D + ((((col >> 3) ^ (row & (CPRo - 1))) << 3) | (col & 7));
+  };
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -478,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
       uint2 w;
       w.x = pack_bf16(acc_o[db][4 * g4 + 0] * inv_l, acc_o[db][4 * g4 + 1] * inv_l);
       w.y = pack_bf16(acc_o[db][4 * g4 + 2] * inv_l, acc_o[db][4 * g4 + 3] * inv_l);
-      *reinterpret_cast<uint2 *>(ost + lq * OP + d) = w;
+      *reinterpret_cast<uint2 *>(ost + ost_off(lq, d)) = w;
     }
   if (a.lse && lh == 0 && my_row < n_cls) {
     const long long t_abs = rho + (long long)dil * my_row;
@@ -495,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const FwdArgs a, const Glob
     const int c = lane % LPR;
     const int r = row0 + rr;
     if (r < n_cls) {
-      const U4 u = *reinterpret_cast<const U4 *>(ost + rr * OP + c * 8);
+      const U4 u = *reinterpret_cast<const U4 *>(ost + ost_off(rr, c * 8));
       const long long t_abs = rho + (long long)dil * r;
       *reinterpret_cast<U4 *>(og + (long long)b * a.q_sb + t_abs * a.q_st + (long long)h * D + c * 8) = u;
     }

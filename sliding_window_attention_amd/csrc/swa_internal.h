@@ -114,7 +114,7 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
   return x * q + (x < rem ? x : rem) + idx;
 }
 
-constexpr int kBN = 64;          // key tile (columns) of the bf16 MFMA kernels
+constexpr int kBN = 32;          // key tile (columns) of the bf16 MFMA kernels
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kRowsPerWave = 32; // query rows per wave (one 32x32 MFMA block)
 

@@ -120,10 +120,10 @@ def test_cache_write_and_debug_validation():
 
 
 def test_tile_config():
-    assert bd.tile_config("p", 32, 8, 128) == (32, 64)     # 4 query heads share a K/V tile
-    assert bd.tile_config("p", 32, 16, 128) == (64, 64)
-    assert bd.tile_config("p", 12, 12, 64) == (128, 64)
-    assert bd.tile_config("l", 12, 12, 64) == (128, 64)
+    assert bd.tile_config("p", 32, 8, 128) == (32, 32)     # 4 query heads share a K/V tile
+    assert bd.tile_config("p", 32, 16, 128) == (64, 32)
+    assert bd.tile_config("p", 12, 12, 64) == (128, 32)
+    assert bd.tile_config("l", 12, 12, 64) == (128, 32)
 
 
 # ------------------------------------------------------------ schedule vs brute force
