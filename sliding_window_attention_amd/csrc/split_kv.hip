@@ -187,22 +187,45 @@ __global__ __launch_bounds__(256) void split_kernel(const SplitArgs a, const Glo
   }
 }
 
-// One workgroup of D threads per (query, kv head, batch).
+// One workgroup of D threads per (query, kv head, batch).  The S partial
+// states are read in parallel (one split per thread), reduced across the
+// workgroup, then every thread merges its output column over all splits.
+template <int D>
+__device__ inline float block_reduce(float x, bool is_max, float *red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float y = __shfl_xor(x, o);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  if constexpr (D > 64) {
+    const int wv = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wv] = x;
+    __syncthreads();
+    x = is_max ? fmaxf(red[0], red[1]) : red[0] + red[1];
+    __syncthreads();
+  }
+  return x;
+}
+
 template <int D, bool F32, bool DECODE>
 __global__ __launch_bounds__(128) void combine_kernel(const SplitArgs a, const GlobalList gl, int G) {
+  __shared__ float red[2];
   const int qi = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int d = threadIdx.x;
   const long long base = (((long long)b * a.NKV + kvh) * a.NQ + qi) * a.S;
-  float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.ws[(base + s) * (D + 2) + D]);
+  const float *ws = a.ws + base * (D + 2);
+  float m_loc = -INFINITY;
+  for (int s = d; s < a.S; s += D) m_loc = fmaxf(m_loc, ws[s * (D + 2) + D]);
+  const float M = block_reduce<D>(m_loc, true, red);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    const float *p = a.ws + (base + s) * (D + 2);
-    const float w = __builtin_amdgcn_exp2f(p[D] - Mu);
-    L = fmaf(w, p[D + 1], L);
-    acc = fmaf(w, p[d], acc);
-  }
+  float l_loc = 0.f;
+  for (int s = d; s < a.S; s += D)
+    l_loc = fmaf(__builtin_amdgcn_exp2f(ws[s * (D + 2) + D] - Mu), ws[s * (D + 2) + D + 1], l_loc);
+  const float L = block_reduce<D>(l_loc, false, red);
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < a.S; ++s)
+    acc = fmaf(__builtin_amdgcn_exp2f(ws[s * (D + 2) + D] - Mu), ws[s * (D + 2) + d], acc);
   const float out = (L > 0.f) ? acc / L : 0.f;
   long long row;  // output row offset
   if constexpr (DECODE) row = b * a.o_sb + kvh * a.o_sh + (long long)qi * a.o_sq;
