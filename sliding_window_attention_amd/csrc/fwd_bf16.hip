@@ -1,9 +1,12 @@
 // fwd_bf16.hip — banded attention forward on bf16 MFMA for gfx950.
 //
-// One workgroup (4 waves) owns one query tile and visits only the key tiles
-// that intersect the band ([PP] §6.1/§6.3: only banded entries are computed;
-// [ST] "The Mechanism": out-of-window key/value blocks are skipped).  Each
-// wave owns 32 query rows of one head.  Per key tile of 64 columns:
+// One workgroup owns one query tile and visits only the key tiles that
+// intersect the band ([PP] §6.1/§6.3: only banded entries are computed; [ST]
+// "The Mechanism": out-of-window key/value blocks are skipped).  Each wave owns
+// 32 query rows of one head; the waves of a workgroup share one key/value head
+// (P query heads x NW/P row blocks), so every staged K/V tile feeds NW waves.
+// A wave skips the staged tiles outside its own rows' band.  Per key tile of
+// 32 columns:
 //
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in VGPRs (B)
 //   mask             only on tiles the schedule marks as partial
@@ -72,7 +75,6 @@ struct Geo {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;      // rows per DMA wave-instruction (4 or 8)
   static constexpr int NI = kBN / RPI;         // DMA instructions per tile and tensor
-  static constexpr int NIW = NI / kWaves;      // ... per wave
   static constexpr int TILE_B = kBN * ROWB;    // bytes per K (or V) tile
 };
 
@@ -161,24 +163,30 @@ __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
 
 // ---- the kernel ------------------------------------------------------------------
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 // Largest growth (log2 units) of a row max tolerated before the running
 // reference max is raised and O, l are rescaled.
 constexpr float kLazy = 8.f;
 
-template <int D, bool SYM>
-__global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const GlobalList gl) {
-  // Row-major K and V tiles (swizzled chunks), two stages each.  Separate
-  // arrays let the compiler see that a DMA into one stage never aliases the
-  // operand reads of the other, so no wait is placed in front of those reads.
-  __shared__ __attribute__((aligned(1024))) char lk0[Geo<D>::TILE_B];
-  __shared__ __attribute__((aligned(1024))) char lk1[Geo<D>::TILE_B];
-  __shared__ __attribute__((aligned(1024))) char lv0[Geo<D>::TILE_B];
-  __shared__ __attribute__((aligned(1024))) char lv1[Geo<D>::TILE_B];
+// NW waves per workgroup; three waves per SIMD (12 per CU) bound the registers.
+template <int D, bool SYM, int NW>
+__global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
+    const FwdArgs a, const GlobalList gl) {
+  using Gm = Geo<D>;
+  // Two stages, each a row-major K tile followed by a V tile (swizzled
+  // chunks); after the loop the same memory stages the output rows.
+  constexpr int STAGE_B = 2 * Gm::TILE_B;
+  constexpr int OST_B = NW * kRowsPerWave * D * 2;
+  constexpr int SMEM_B = (2 * STAGE_B > OST_B) ? 2 * STAGE_B : OST_B;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_B];
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
   constexpr int KB = kBN / 32;   // 32-key blocks of S^T per tile
   constexpr int PK = kBN / 16;   // 16-key k-steps of the PV product per tile
-  using Gm = Geo<D>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -268,53 +276,68 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const Glob
   const int n_win = tr.hi - tr.lo + 1;
   const int n_glob = SYM ? ceil_div(a.G, kBN) : 0;
   const int n_tiles = n_win + n_glob;
+  // this wave's valid rows [row0, w_last] and the window tiles they need
+  const int w_last = min(row0 + kRowsPerWave, n_cls) - 1;
+  TileRange wr{1, 0};
+  if (w_last >= row0) {
+    if constexpr (!SYM) wr = causal_tile_range(row0, w_last, a.W, kBN);
+    else wr = sym_tile_range(row0, w_last, a.W, n_cls, kBN);
+  }
+  wr.lo = uni(wr.lo);
+  wr.hi = uni(wr.hi);
+  const bool has_rows = w_last >= row0;
 
-  // -------- DMA addressing.  Wave instruction i of a tile covers rows
-  // i*RPI .. i*RPI+RPI-1; lane l lands at LDS byte 16*l of that 1 KB, i.e. row
-  // i*RPI + l/CPR, physical chunk l%CPR, so it loads logical chunk
-  // (l%CPR) ^ swz(row).  Rows of a window tile are consecutive class rows, so
-  // the per-lane byte offsets are fixed and each tile adds a uniform base.
+  // -------- DMA addressing.  A stage takes 2*NI wave instructions of 1 KB:
+  // instruction i < NI copies K rows i*RPI .. i*RPI+RPI-1, instruction NI + i
+  // the same V rows, to stage byte 1024*i.  Lane l lands at byte 16*l of its
+  // instruction's 1 KB, i.e. row i*RPI + l/CPR, physical chunk l%CPR, so it
+  // loads logical chunk (l%CPR) ^ swz(row).  Wave w issues instructions
+  // w, w+NW, ...  Rows of a window tile are consecutive class rows, so the
+  // per-lane byte offsets are fixed and each tile adds a uniform base.
+  constexpr int NSLOT = (2 * Gm::NI + NW - 1) / NW;
   const long long rs_b = k_rowstride * 2;  // bytes between consecutive class rows
-  uint32_t koff[Gm::NIW], voff[Gm::NIW];
+  uint32_t loff[NSLOT];
 #pragma unroll
-  for (int t = 0; t < Gm::NIW; ++t) {
-    const int r = (wave * Gm::NIW + t) * Gm::RPI + lane / Gm::CPR;
+  for (int t = 0; t < NSLOT; ++t) {
+    const int i = wave + t * NW;
+    const int r = (i % Gm::NI) * Gm::RPI + lane / Gm::CPR;
     const int p = lane % Gm::CPR;
-    koff[t] = (uint32_t)(r * rs_b) + (p ^ swz_k<D>(r)) * 16;
-    voff[t] = (uint32_t)(r * rs_b) + (p ^ swz_v<D>(r)) * 16;
+    loff[t] = (uint32_t)(r * rs_b) + (p ^ (i >= Gm::NI ? swz_v<D>(r) : swz_k<D>(r))) * 16;
   }
   const char *kb8 = reinterpret_cast<const char *>(kbase);
   const char *vb8 = reinterpret_cast<const char *>(vbase);
-  // DMA of the K (which = 0) or V (which = 1) rows of tile j (window tiles
-  // j < n_win, then tiles of global keys) into the LDS tile at `dst`.
-  auto issue = [&](int j, uint32_t dst, int which) {
-    const uint32_t ld = dst + wave * Gm::NIW * 1024;
-    const char *g8 = which ? vb8 : kb8;
-    uint32_t off[Gm::NIW];
-    if (j < n_win && (tr.lo + j) * kBN + kBN <= n_cls) {
-      // whole tile inside the class: uniform base + fixed lane offsets
-      const long long base = (k_rho + (long long)(tr.lo + j) * kBN * k_rowstride) * 2;
+  // DMA of the K and V rows of tile j (window tiles j < n_win, then tiles of
+  // global keys) into the stage at LDS address `stage`.
+  auto issue = [&](int j, uint32_t stage) {
+    const bool whole = j < n_win && (tr.lo + j) * kBN + kBN <= n_cls;
+    const long long base = (k_rho + (long long)(tr.lo + j) * kBN * k_rowstride) * 2;
 #pragma unroll
-      for (int t = 0; t < Gm::NIW; ++t) off[t] = which ? voff[t] : koff[t];
-      dma_tile<Gm::NIW>(g8 + base, off, ld);
-    } else {
-      // ragged last tile (rows clamped to the last valid row; the mask
-      // removes them) or a tile of global keys (absolute positions)
-#pragma unroll
-      for (int t = 0; t < Gm::NIW; ++t) {
-        const int r = (wave * Gm::NIW + t) * Gm::RPI + lane / Gm::CPR;
-        const int p = lane % Gm::CPR;
-        long long o;
-        if (j < n_win) {
-          const int sr = min((tr.lo + j) * kBN + r, n_cls - 1);
-          o = (k_rho + (long long)sr * k_rowstride) * 2;
+    for (int t = 0; t < NSLOT; ++t) {
+      const int i = wave + t * NW;
+      if (i < 2 * Gm::NI) {
+        const bool isv = i >= Gm::NI;
+        const char *g8 = isv ? vb8 : kb8;
+        const uint32_t ld = stage + (uint32_t)i * 1024u;
+        if (whole) {
+          // whole tile inside the class: uniform base + fixed lane offsets
+          dma_tile<1>(g8 + base, &loff[t], ld);
         } else {
-          const int u = min((j - n_win) * kBN + r, a.G - 1);
-          o = (long long)gl.idx[b * a.G + u] * a.k_st * 2;
+          // ragged last tile (rows clamped to the last valid row; the mask
+          // removes them) or a tile of global keys (absolute positions)
+          const int r = (i % Gm::NI) * Gm::RPI + lane / Gm::CPR;
+          const int p = lane % Gm::CPR;
+          long long o;
+          if (j < n_win) {
+            const int sr = min((tr.lo + j) * kBN + r, n_cls - 1);
+            o = (k_rho + (long long)sr * k_rowstride) * 2;
+          } else {
+            const int u = min((j - n_win) * kBN + r, a.G - 1);
+            o = (long long)gl.idx[b * a.G + u] * a.k_st * 2;
+          }
+          const uint32_t off = (uint32_t)o + (p ^ (isv ? swz_v<D>(r) : swz_k<D>(r))) * 16;
+          dma_tile<1>(g8, &off, ld);
         }
-        off[t] = (uint32_t)o + (which ? (p ^ swz_v<D>(r)) : (p ^ swz_k<D>(r))) * 16;
       }
-      dma_tile<Gm::NIW>(g8, off, ld);
     }
   };
 
@@ -322,8 +345,11 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const Glob
   // K (A operand of S^T): lane reads row 32kb + lq, logical chunk 2kk + lh.
   uint32_t kop[KS_QK];
 #pragma unroll
-  for (int kk = 0; kk < KS_QK; ++kk)
+  for (int kk = 0; kk < KS_QK; ++kk) {
     kop[kk] = lq * Gm::ROWB + (((2 * kk + lh) ^ swz_k<D>(lq)) * 16);
+    // kept whole, so each read is one ds_read with the stage as its offset
+    asm volatile("" : "+v"(kop[kk]));
+  }
   // V^T (A operand of O^T): two transposing reads per 16-key step.  In each
   // group of 16 lanes, source lane s addresses row 16kk + 4hh + s/4 at columns
   // 32db + 16dg + 4(s%4) .. +3, so output lane i of the group receives column
@@ -339,6 +365,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const Glob
     for (int db = 0; db < DB; ++db) {
       const int c = 4 * db + 2 * dg + ((sl >> 1) & 1);
       vop[db] = row * Gm::ROWB + ((c ^ swz_v<D>(row)) * 16) + 8 * (sl & 1);
+      asm volatile("" : "+v"(vop[db]));
     }
   }
 
@@ -419,11 +446,12 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const Glob
       }
     }
   };
+  // every (valid row of this wave, key) pair of window tile j attended?
   auto tile_full = [&](int j) {
     if (j >= n_win) return false;  // tiles of global keys are always masked
     const int kj = tr.lo + j;
-    if constexpr (!SYM) return causal_tile_full(tile_row0, t1_valid, kj, kBN, a.W, n_cls);
-    else return sym_tile_full(tile_row0, t1_valid, kj, kBN, a.W, n_cls);
+    if constexpr (!SYM) return causal_tile_full(row0, w_last, kj, kBN, a.W, n_cls);
+    else return sym_tile_full(row0, w_last, kj, kBN, a.W, n_cls);
   };
   // mask of a partial tile: window predicate, or for a tile of global keys
   // the globals not already inside this row's (dilated) window
@@ -450,38 +478,40 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(const FwdArgs a, const Glob
       }
   };
 
+  const uint32_t a_s0 = lds_addr(smem);
   // ---- main loop: tile j+1 is copied into the other stage while tile j is
-  // computed; one barrier per tile.
-  const uint32_t a_k0 = lds_addr(lk0), a_k1 = lds_addr(lk1);
-  const uint32_t a_v0 = lds_addr(lv0), a_v1 = lds_addr(lv1);
-  issue(0, a_k0, 0);
-  issue(0, a_v0, 1);
-  wait_dma();
-  __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_tiles) {
-      issue(j + 1, st ? a_k0 : a_k1, 0);
-      issue(j + 1, st ? a_v0 : a_v1, 1);
+  // computed; one barrier per tile.  Unrolled by the two stages so every LDS
+  // operand address is a fixed register plus an immediate offset.
+  auto step = [&](int j, auto stage) {
+    constexpr int st = decltype(stage)::value;
+    if (j + 1 < n_tiles) issue(j + 1, a_s0 + (st ? 0u : (uint32_t)STAGE_B));
+    const int kj = tr.lo + j;
+    if (has_rows && (j >= n_win || (kj >= wr.lo && kj <= wr.hi))) {
+      const char *ks = smem + st * STAGE_B;
+      f32x16 sv[KB];
+      U4 pu[PK];
+      qk(ks, sv);
+      if (!tile_full(j)) mask(j, sv);
+      rescale(rowmax(sv));
+      exp_pack(sv, pu);
+      pv(ks + Gm::TILE_B, pu);
     }
-    f32x16 sv[KB];
-    U4 pu[PK];
-    qk(st ? lk1 : lk0, sv);
-    if (!tile_full(j)) mask(j, sv);
-    rescale(rowmax(sv));
-    exp_pack(sv, pu);
-    pv(st ? lv1 : lv0, pu);
     wait_dma();
     __syncthreads();
+  };
+  issue(0, a_s0);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, IntC<0>{});
+    if (j + 1 < n_tiles) step(j + 1, IntC<1>{});
   }
 
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
   const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
   // Each wave stages its 32 rows (row-major, 16-byte chunks XOR-swizzled by
-  // row, no padding) in one of the four idle tile buffers.
-  static_assert(kRowsPerWave * D * 2 <= Geo<D>::TILE_B, "O staging must fit a tile buffer");
-  char *stage_buf = wave == 0 ? lk0 : wave == 1 ? lk1 : wave == 2 ? lv0 : lv1;
-  uint16_t *ost = reinterpret_cast<uint16_t *>(stage_buf);
+  // row, no padding) in its own slice of the now idle stage memory.
+  uint16_t *ost = reinterpret_cast<uint16_t *>(smem + wave * kRowsPerWave * D * 2);
   constexpr int CPRo = D / 8;  // 16-byte chunks per staged row
   auto ost_off = [&](int row, int col) {  // element offset of (row, col)
     return row * D + ((((col >> 3) ^ (row & (CPRo - 1))) << 3) | (col & 7));
@@ -524,13 +554,15 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool symmetric, int D, const Global
                            hipStream_t st) {
   const int nblk = symmetric ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
   if (nblk <= 0) return hipSuccess;
-  dim3 grid(nblk), block(256);
+  constexpr int NWC = SWA_FWD_WAVES;
+  if (a.NW != (symmetric ? 4 : NWC)) return hipErrorInvalidValue;
+  dim3 grid(nblk), block(64 * a.NW);
   if (!symmetric) {
-    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, false>), grid, block, 0, st, a, *gl);
-    else hipLaunchKernelGGL((fwd_kernel<64, false>), grid, block, 0, st, a, *gl);
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, false, NWC>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, false, NWC>), grid, block, 0, st, a, *gl);
   } else {
-    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, true>), grid, block, 0, st, a, *gl);
-    else hipLaunchKernelGGL((fwd_kernel<64, true>), grid, block, 0, st, a, *gl);
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, true, 4>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, true, 4>), grid, block, 0, st, a, *gl);
   }
   return hipGetLastError();
 }

@@ -72,9 +72,9 @@ swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *
   if (!BM || !BN || H_q < 1 || H_kv < 1 || H_q % H_kv) return SWA_ERR_INVALID;
   if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
   if (entry == 'p') {
-    *BM = kRowsPerWave * kWaves / prefill_pack(H_q, H_kv);
+    *BM = kRowsPerWave * fwd_waves(false) / prefill_pack(H_q, H_kv);
   } else if (entry == 'l') {
-    *BM = kRowsPerWave * kWaves;
+    *BM = kRowsPerWave * fwd_waves(true);
   } else {
     return SWA_ERR_INVALID;
   }
@@ -129,7 +129,8 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
   a.P = prefill_pack(H_q, H_kv);
-  a.BM = kRowsPerWave * kWaves / a.P;
+  a.NW = fwd_waves(false);
+  a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (T + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
   GlobalList gl;
@@ -241,7 +242,8 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   a.sl2 = scale * kLog2e;
   a.group = 1;
   a.P = 1;
-  a.BM = kRowsPerWave * kWaves;
+  a.NW = fwd_waves(true);
+  a.BM = kRowsPerWave * a.NW;
   a.G = G;
   long long tiles = 0;
   for (int h = 0; h < H; ++h) {

@@ -115,8 +115,16 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
 }
 
 constexpr int kBN = 32;          // key tile (columns) of the bf16 MFMA kernels
-constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kRowsPerWave = 32; // query rows per wave (one 32x32 MFMA block)
+
+// Waves per workgroup of the bf16 kernels.  Every wave of a workgroup reads
+// the same staged K/V tiles, so more waves per workgroup means fewer bytes
+// copied into LDS per FLOP.  Causal prefill runs 12 waves (one workgroup per
+// CU, three waves per SIMD) or 4; symmetric mode 4.
+#ifndef SWA_FWD_WAVES
+#define SWA_FWD_WAVES 4
+#endif
+inline int fwd_waves(bool symmetric) { return symmetric ? 4 : SWA_FWD_WAVES; }
 
 // Heads packed into one workgroup for the causal kernel: waves of one
 // workgroup take query heads that share a key/value head, so a staged K/V tile
@@ -144,6 +152,7 @@ struct FwdArgs {
   int P, group;          // heads per workgroup, H_q / H_kv
   int n_qt, n_hg;        // causal: query tiles per head group, head groups
   int BM;                // query rows per workgroup
+  int NW;                // waves per workgroup
   // symmetric (Longformer) mode
   int G;                       // globals per batch row
   int tiles_per_batch;         // sum over heads of class tiles

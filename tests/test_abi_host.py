@@ -120,7 +120,8 @@ def test_cache_write_and_debug_validation():
 
 
 def test_tile_config():
-    assert bd.tile_config("p", 32, 8, 128) == (32, 32)     # 4 query heads share a K/V tile
+    # 4 waves of 32 rows; 4 (2, 1) query heads share a K/V tile
+    assert bd.tile_config("p", 32, 8, 128) == (32, 32)
     assert bd.tile_config("p", 32, 16, 128) == (64, 32)
     assert bd.tile_config("p", 12, 12, 64) == (128, 32)
     assert bd.tile_config("l", 12, 12, 64) == (128, 32)
@@ -163,16 +164,22 @@ def test_schedule_at_kernel_tiling_small():
 
 
 def test_schedule_steady_state_counts_full_size():
-    # full-size causal workload (T=16384, W=4096) at the kernel tiling: every
-    # steady-state query tile visits W/BN + 1 key tiles, exactly two partial;
-    # ramp tiles have only the diagonal tile partial.
+    # full-size causal workload (T=16384, W=4096) at the kernel tiling (BM a
+    # multiple of BN): every steady-state query tile visits (W + BM)/BN key
+    # tiles, BM/BN partial ones at each edge of the band; ramp tiles have only
+    # the BM/BN diagonal tiles partial.
     BM, BN = bd.tile_config("p", 32, 8, 128)
+    assert BM % BN == 0
+    nd = BM // BN
     T, W = 16384, 4096
     tr = np.array(bd.band_tiles(0, T, W, BM, BN))
     for qi in range(T // BM):
         rows = tr[tr[:, 0] == qi]
         m0 = qi * BM
         if m0 + BM <= W:
-            assert rows[:, 2].sum() == 1 and rows[-1, 2] == 1
-        else:
-            assert len(rows) == W // BN + 1 and rows[:, 2].sum() == 2
+            assert rows[:, 2].sum() == nd and rows[-nd:, 2].all()
+        elif m0 >= W:
+            assert len(rows) == (W + BM) // BN and rows[:, 2].sum() == 2 * nd
+            assert rows[:nd, 2].all() and rows[-nd:, 2].all()
+        else:  # band reaches key 0 for some rows of the tile but not all
+            assert rows[0, 1] == 0 and rows[-nd:, 2].all()
