@@ -16,6 +16,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -61,6 +62,28 @@ def longformer_pairs(T, r, dil, globals_):
             extra += (~inside).astype(np.int64)
         total += int(np.where(is_g, T, win + extra).sum())
     return total
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per dispatch of one kernel, as recorded from rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by a plain-copy calibration) in
+    profiles/hbm_traffic.json.  None when the file is missing, the kernel was
+    not recorded, or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        k = rec["kernels"][kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    return dict(bytes=k["read_bytes"] + k["write_bytes"], read_bytes=k["read_bytes"],
+                write_bytes=k["write_bytes"])
 
 
 def time_launches(fn, steps, warmup):
@@ -182,13 +205,15 @@ def main():
         extra["decode"] = dict(
             workload="ring decode B=64 W=4096 Hq=32 Hkv=8 d_h=128 bf16, cur_pos in [4096, 32768)",
             value=round(r4["gbs"], 1), unit="GB/s", ms=round(r4["ms"], 4),
-            frac_hbm_peak=round(r4["gbs"] / PEAK_HBM_GBS, 4), bytes=r4["bytes"])
+            frac_hbm_peak=round(r4["gbs"] / PEAK_HBM_GBS, 4), bytes=r4["bytes"],
+            traffic_split_pass=measured_traffic("split_mfma_kernel<128, 4, true>@262144"))
     if args.only in ("all", "longformer"):
         r5 = bench_longformer(inp.C5, max(20, args.steps), args.warmup)
         extra["longformer"] = dict(
             workload="Longformer B=8 T=4096 H=12 d_h=64 r=256, dilation 2 on heads 8-11, globals {0,8}",
             value=round(r5["tflops"], 2), unit="TFLOP/s", ms=round(r5["ms"], 4),
-            frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"])
+            frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"],
+            traffic_local_pass=measured_traffic("fwd_kernel<64, true, 4>@786432"))
 
     if main_r is None:
         print(json.dumps({"partial": args.only, "extra": extra}), flush=True)
@@ -198,6 +223,7 @@ def main():
         cpu = cpu_baseline(c2)
 
     ach = main_r["tflops"]
+    tr = measured_traffic("fwd_kernel<128, false, 4>@1048576")
     out = {
         "metric": METRIC,
         "value": round(ach, 2),
@@ -216,9 +242,11 @@ def main():
                    "accumulate": "fp32"},
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": None if tr is None else tr["bytes"],
+                     "traffic_detail": tr,
                      "kernel": "fwd_kernel<128, causal>",
-                     "algorithmic_flop_per_launch": main_r["flops"]},
+                     "algorithmic_flop_per_launch": main_r["flops"],
+                     "algorithmic_bytes_per_launch": main_r["bytes"]},
         "cpu_baseline": cpu,
         "extra": extra,
     }
