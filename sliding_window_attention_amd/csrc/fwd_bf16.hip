@@ -74,8 +74,9 @@ struct Geo {
   static constexpr int ROWB = 2 * D;           // bytes per K/V row
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;      // rows per DMA wave-instruction (4 or 8)
-  static constexpr int NI = kBN / RPI;         // DMA instructions per tile and tensor
-  static constexpr int TILE_B = kBN * ROWB;    // bytes per K (or V) tile
+  static constexpr int BN = key_tile(D);       // keys per tile
+  static constexpr int NI = BN / RPI;          // DMA instructions per tile and tensor
+  static constexpr int TILE_B = BN * ROWB;     // bytes per K (or V) tile
 };
 
 // Physical chunk = logical chunk ^ swz(row).
@@ -149,9 +150,23 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
   }
 }
 
-// Drain this wave's copies.  Inline assembly: the compiler does not know about
-// the copies and would drop a wait it considers redundant.
-__device__ inline void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most n of this wave's vector-memory operations are still in
+// flight (they complete in issue order), i.e. every copy except the n most
+// recent has landed in LDS.  Inline assembly: the compiler does not know about
+// the copies and would drop a wait it considers redundant.  n is wave-uniform.
+__device__ inline void wait_dma_keep(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+  }
+}
 
 __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)p0);
@@ -177,20 +192,24 @@ template <int D, bool SYM, int NW>
 __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
     const FwdArgs a, const GlobalList gl) {
   using Gm = Geo<D>;
-  // Two stages, each a row-major K tile followed by a V tile (swizzled
-  // chunks); after the loop the same memory stages the output rows.
+  // NST stages, each a row-major K tile followed by a V tile (swizzled
+  // chunks); copies run NST-1 tiles ahead of the compute.  After the loop the
+  // same memory stages the output rows.
   constexpr int STAGE_B = 2 * Gm::TILE_B;
+  constexpr int NST = 2;
   constexpr int OST_B = NW * kRowsPerWave * D * 2;
-  constexpr int SMEM_B = (2 * STAGE_B > OST_B) ? 2 * STAGE_B : OST_B;
+  constexpr int SMEM_B = (NST * STAGE_B > OST_B) ? NST * STAGE_B : OST_B;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_B];
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
-  constexpr int KB = kBN / 32;   // 32-key blocks of S^T per tile
-  constexpr int PK = kBN / 16;   // 16-key k-steps of the PV product per tile
+  constexpr int BN = Gm::BN;     // keys per tile
+  constexpr int KB = BN / 32;    // 32-key blocks of S^T per tile
+  constexpr int PK = BN / 16;    // 16-key k-steps of the PV product per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  __builtin_assume(wave >= 0 && wave < NW);
   const int lq = lane & 31, lh = lane >> 5;
 
   // -------- work decode
@@ -269,19 +288,19 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
 
   // -------- schedule
   TileRange tr;
-  if constexpr (!SYM) tr = causal_tile_range(tile_row0, t1_valid, a.W, kBN);
-  else tr = sym_tile_range(tile_row0, t1_valid, a.W, n_cls, kBN);
+  if constexpr (!SYM) tr = causal_tile_range(tile_row0, t1_valid, a.W, BN);
+  else tr = sym_tile_range(tile_row0, t1_valid, a.W, n_cls, BN);
   tr.lo = uni(tr.lo);
   tr.hi = uni(tr.hi);
   const int n_win = tr.hi - tr.lo + 1;
-  const int n_glob = SYM ? ceil_div(a.G, kBN) : 0;
+  const int n_glob = SYM ? ceil_div(a.G, BN) : 0;
   const int n_tiles = n_win + n_glob;
   // this wave's valid rows [row0, w_last] and the window tiles they need
   const int w_last = min(row0 + kRowsPerWave, n_cls) - 1;
   TileRange wr{1, 0};
   if (w_last >= row0) {
-    if constexpr (!SYM) wr = causal_tile_range(row0, w_last, a.W, kBN);
-    else wr = sym_tile_range(row0, w_last, a.W, n_cls, kBN);
+    if constexpr (!SYM) wr = causal_tile_range(row0, w_last, a.W, BN);
+    else wr = sym_tile_range(row0, w_last, a.W, n_cls, BN);
   }
   wr.lo = uni(wr.lo);
   wr.hi = uni(wr.hi);
@@ -309,8 +328,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   // DMA of the K and V rows of tile j (window tiles j < n_win, then tiles of
   // global keys) into the stage at LDS address `stage`.
   auto issue = [&](int j, uint32_t stage) {
-    const bool whole = j < n_win && (tr.lo + j) * kBN + kBN <= n_cls;
-    const long long base = (k_rho + (long long)(tr.lo + j) * kBN * k_rowstride) * 2;
+    const bool whole = j < n_win && (tr.lo + j) * BN + BN <= n_cls;
+    const long long base = (k_rho + (long long)(tr.lo + j) * BN * k_rowstride) * 2;
 #pragma unroll
     for (int t = 0; t < NSLOT; ++t) {
       const int i = wave + t * NW;
@@ -328,10 +347,10 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           const int p = lane % Gm::CPR;
           long long o;
           if (j < n_win) {
-            const int sr = min((tr.lo + j) * kBN + r, n_cls - 1);
+            const int sr = min((tr.lo + j) * BN + r, n_cls - 1);
             o = (k_rho + (long long)sr * k_rowstride) * 2;
           } else {
-            const int u = min((j - n_win) * kBN + r, a.G - 1);
+            const int u = min((j - n_win) * BN + r, a.G - 1);
             o = (long long)gl.idx[b * a.G + u] * a.k_st * 2;
           }
           const uint32_t off = (uint32_t)o + (p ^ (isv ? swz_v<D>(r) : swz_k<D>(r))) * 16;
@@ -450,41 +469,66 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   auto tile_full = [&](int j) {
     if (j >= n_win) return false;  // tiles of global keys are always masked
     const int kj = tr.lo + j;
-    if constexpr (!SYM) return causal_tile_full(row0, w_last, kj, kBN, a.W, n_cls);
-    else return sym_tile_full(row0, w_last, kj, kBN, a.W, n_cls);
+    if constexpr (!SYM) return causal_tile_full(row0, w_last, kj, BN, a.W, n_cls);
+    else return sym_tile_full(row0, w_last, kj, BN, a.W, n_cls);
   };
+  // Attended keys of row my_row inside the window, [lo_key, hi_key]: the
+  // causal predicate (t-W < s <= t) or the symmetric one (|i-j| <= r), cut at
+  // the class length.
+  const int lo_key = SYM ? my_row - a.W : my_row - a.W + 1;
+  const int hi_key = min(SYM ? my_row + a.W : my_row, n_cls - 1);
   // mask of a partial tile: window predicate, or for a tile of global keys
   // the globals not already inside this row's (dilated) window
   auto mask = [&](int j, f32x16 *sv) {
-    const int key_base = (j < n_win) ? (tr.lo + j) * kBN : (j - n_win) * kBN;
+    if (j < n_win) {
+      // key of element (kb, e) = tile base + 4*lh + c(kb, e); compare c with
+      // this lane's bounds shifted to the same origin
+      const int base = (tr.lo + j) * BN + 4 * lh;
+      const int lo = lo_key - base, hi = hi_key - base;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+          if (c < lo || c > hi) sv[kb][e] = -INFINITY;
+        }
+      return;
+    }
+    // Tile of global keys: column c holds global u0 + c.  Bit c of okb is set
+    // when that global exists and is not already inside row my_row's
+    // (dilated) window, where the window tiles count it.  The loop runs over
+    // the tile's globals only (often just a few).
+    const int u0 = (j - n_win) * BN;
+    const int ng = min(a.G - u0, BN);
+    const int i_abs = rho + dil * my_row;
+    uint64_t okb = 0;
+    for (int c = 0; c < ng; ++c) {
+      const int g = gl.idx[b * a.G + u0 + c];
+      if (!dilated_in(i_abs, g, a.W, dil)) okb |= 1ull << c;
+    }
+    okb >>= 4 * lh;  // this lane's columns are 4*lh + c(kb, e)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int kk = key_base + kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-        bool ok;
-        if (j < n_win) {
-          if constexpr (!SYM) ok = causal_in(my_row, kk, a.W) && kk < n_cls;
-          else ok = sym_in(my_row, kk, a.W) && kk < n_cls;
-        } else {
-          ok = false;
-          if (kk < a.G) {
-            const int g = gl.idx[b * a.G + kk];
-            const int i_abs = rho + dil * my_row;
-            ok = !dilated_in(i_abs, g, a.W, dil);
-          }
-        }
-        if (!ok) sv[kb][e] = -INFINITY;
+        const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+        if (!((okb >> c) & 1)) sv[kb][e] = -INFINITY;
       }
   };
 
   const uint32_t a_s0 = lds_addr(smem);
-  // ---- main loop: tile j+1 is copied into the other stage while tile j is
-  // computed; one barrier per tile.  Unrolled by the two stages so every LDS
+  // ---- main loop: tile j is computed from stage j % NST while the copies of
+  // tiles j+1 .. j+NST-1 are in flight.  Step j waits for its own tile and
+  // barriers (so every wave is also done with tile j-1), then reuses tile
+  // j-1's stage for tile j+NST-1.  Unrolled by the NST stages so every LDS
   // operand address is a fixed register plus an immediate offset.
+  constexpr int NCOPY = NSLOT;  // copies per wave and tile
+  static_assert((2 * Gm::NI) % NW == 0, "every wave issues the same number of copies");
   auto step = [&](int j, auto stage) {
     constexpr int st = decltype(stage)::value;
-    if (j + 1 < n_tiles) issue(j + 1, a_s0 + (st ? 0u : (uint32_t)STAGE_B));
+    wait_dma_keep(min(n_tiles - 1 - j, NST - 2) * NCOPY);
+    __syncthreads();
+    if (j + NST - 1 < n_tiles) issue(j + NST - 1, a_s0 + (uint32_t)(((st + NST - 1) % NST) * STAGE_B));
     const int kj = tr.lo + j;
     if (has_rows && (j >= n_win || (kj >= wr.lo && kj <= wr.hi))) {
       const char *ks = smem + st * STAGE_B;
@@ -496,16 +540,21 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       exp_pack(sv, pu);
       pv(ks + Gm::TILE_B, pu);
     }
-    wait_dma();
-    __syncthreads();
   };
-  issue(0, a_s0);
-  wait_dma();
-  __syncthreads();
-  for (int j = 0; j < n_tiles; j += 2) {
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < n_tiles) issue(p, a_s0 + (uint32_t)(p * STAGE_B));
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  for (int j = 0; j < n_tiles; j += NST) {
     step(j, IntC<0>{});
     if (j + 1 < n_tiles) step(j + 1, IntC<1>{});
+    if constexpr (NST > 2)
+      if (j + 2 < n_tiles) step(j + 2, IntC<2 % NST>{});
+    if constexpr (NST > 3)
+      if (j + 3 < n_tiles) step(j + 3, IntC<3 % NST>{});
   }
+  // other waves may still read the last stage, which the output staging reuses
+  __syncthreads();
 
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
   const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;

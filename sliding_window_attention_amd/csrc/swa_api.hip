@@ -78,7 +78,7 @@ swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *
   } else {
     return SWA_ERR_INVALID;
   }
-  *BN = kBN;
+  *BN = key_tile(d_h);
   return SWA_OK;
 }
 

@@ -114,7 +114,9 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
   return x * q + (x < rem ? x : rem) + idx;
 }
 
-constexpr int kBN = 32;          // key tile (columns) of the bf16 MFMA kernels
+// Key tile (columns) of the bf16 MFMA kernels: 32 keys at d_h = 128, 64 at
+// d_h = 64 (8 KB of K per tile either way).
+__host__ __device__ constexpr int key_tile(int D) { return D == 64 ? 64 : 32; }
 constexpr int kRowsPerWave = 32; // query rows per wave (one 32x32 MFMA block)
 
 // Waves per workgroup of the bf16 kernels.  Every wave of a workgroup reads

@@ -123,8 +123,8 @@ def test_tile_config():
     # 4 waves of 32 rows; 4 (2, 1) query heads share a K/V tile
     assert bd.tile_config("p", 32, 8, 128) == (32, 32)
     assert bd.tile_config("p", 32, 16, 128) == (64, 32)
-    assert bd.tile_config("p", 12, 12, 64) == (128, 32)
-    assert bd.tile_config("l", 12, 12, 64) == (128, 32)
+    assert bd.tile_config("p", 12, 12, 64) == (128, 64)   # 64-key tiles at d_h = 64
+    assert bd.tile_config("l", 12, 12, 64) == (128, 64)
 
 
 # ------------------------------------------------------------ schedule vs brute force
