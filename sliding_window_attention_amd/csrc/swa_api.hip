@@ -26,13 +26,13 @@ bool d_ok(int d) { return d == 64 || d == 128; }
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Number of key chunks for a split-KV launch: enough workgroups to fill the
-// chip (>= 2048), chunks between 64 and the kernel's maximum.
-int choose_splits(long long heads_total, int n_keys) {
-  const int maxc = split_max_chunk();
+// Number of splits for split-KV over n_keys keys per (batch, head): enough
+// workgroups to fill the chip (target), each chunk whole 32-key blocks
+// between 64 keys and maxc.
+int choose_splits(long long heads_total, int n_keys, int maxc, int target) {
   int s_min = (n_keys + maxc - 1) / maxc;
   int s_max = (n_keys + 63) / 64;
-  long long want = (2048 + heads_total - 1) / heads_total;
+  long long want = (target + heads_total - 1) / heads_total;
   int s = (int)std::max<long long>(s_min, std::min<long long>(want, s_max));
   if (s < 1) s = 1;
   int chunk = (n_keys + s - 1) / s;
@@ -40,10 +40,26 @@ int choose_splits(long long heads_total, int n_keys) {
   return (n_keys + chunk - 1) / chunk;
 }
 
-// Keys per split for S splits (whole 32-key blocks, at most the kernel maximum).
-int split_chunk(int n_keys, int S) {
+// Keys per split for S splits (whole 32-key blocks, at most maxc).
+int split_chunk(int n_keys, int S, int maxc) {
   int chunk = (n_keys + S - 1) / S;
-  return std::min(split_max_chunk(), (chunk + 31) / 32 * 32);
+  return std::min(maxc, (chunk + 31) / 32 * 32);
+}
+
+// Split policies.  The fp32 kernel keeps a chunk's scores in LDS (at most
+// split_max_chunk() keys); the bf16 kernel streams its chunk and has no limit,
+// so it takes fewer, longer splits: one round of resident waves.  The fp32
+// policy never gives fewer splits, so it sizes the workspace for both.
+#ifndef SWA_STREAM_TARGET
+#define SWA_STREAM_TARGET 2048
+#endif
+constexpr int kStreamMaxChunk = 1 << 20;
+int splits_for(bool f32, long long heads_total, int n_keys) {
+  return f32 ? choose_splits(heads_total, n_keys, split_max_chunk(), 2048)
+             : choose_splits(heads_total, n_keys, kStreamMaxChunk, SWA_STREAM_TARGET);
+}
+int chunk_for(bool f32, int n_keys, int S) {
+  return split_chunk(n_keys, S, f32 ? split_max_chunk() : kStreamMaxChunk);
 }
 
 swa_status hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
@@ -145,7 +161,7 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
 
 size_t swa_decode_workspace_size(int B, int H_q, int H_kv, int W, int d_h) {
   if (B < 1 || H_q < 1 || H_kv < 1 || W < 1 || H_q % H_kv || !d_ok(d_h)) return 0;
-  const int S = choose_splits((long long)B * H_kv, W);
+  const int S = splits_for(true, (long long)B * H_kv, W);
   return (size_t)B * H_q * S * (d_h + 2) * sizeof(float);
 }
 
@@ -172,8 +188,8 @@ swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const vo
   a.slot_pos = slot_pos; a.cur_pos = cur_pos;
   a.B = B; a.NKV = H_kv; a.NQ = H_q / H_kv;
   a.n_keys = W;
-  a.S = choose_splits((long long)B * H_kv, W);
-  a.chunk = split_chunk(W, a.S);
+  a.S = splits_for(dt == SWA_F32, (long long)B * H_kv, W);
+  a.chunk = chunk_for(dt == SWA_F32, W, a.S);
   a.W = W;
   a.q_sq = d_h; a.q_sh = (long long)a.NQ * d_h; a.q_sb = (long long)H_q * d_h;
   a.o_sq = a.q_sq; a.o_sh = a.q_sh; a.o_sb = a.q_sb;
@@ -203,7 +219,7 @@ swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new, c
 size_t swa_longformer_workspace_size(int B, int T, int H, int d_h, int G) {
   if (B < 1 || T < 1 || H < 1 || G < 0 || !d_ok(d_h)) return 0;
   if (G == 0) return 0;
-  const int S = choose_splits((long long)B * H, T);
+  const int S = splits_for(true, (long long)B * H, T);
   return (size_t)B * H * G * S * (d_h + 2) * sizeof(float);
 }
 
@@ -272,8 +288,8 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   s.ws = static_cast<float *>(workspace);
   s.B = B; s.NKV = H; s.NQ = G;
   s.n_keys = T;
-  s.S = choose_splits((long long)B * H, T);
-  s.chunk = split_chunk(T, s.S);
+  s.S = splits_for(dt == SWA_F32, (long long)B * H, T);
+  s.chunk = chunk_for(dt == SWA_F32, T, s.S);
   s.q_sb = a.q_sb; s.q_sh = d_h; s.q_sq = a.q_st;
   s.o_sb = a.q_sb; s.o_sh = d_h; s.o_sq = a.q_st;
   s.k_sb = a.k_sb; s.k_sh = d_h; s.k_sr = a.k_st;
