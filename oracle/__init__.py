@@ -21,7 +21,7 @@ pages, cited by page title and section.  Short tags used in citations:
 Modules
   index_sets  connectivity sets S_t (causal, symmetric/dilated/global, ring decode)
   attention   masked softmax attention over those sets (+ the dense-mask form)
-  ring        the rolling-buffer KV cache write rule
+  ring        the rolling-buffer KV cache write rule (one token or a chunk)
   tiles       brute-force band-tile classification for a (BM, BN) tiling
 
 Pins: every function here is pinned in ``tests/test_oracle_pins.py`` against the
@@ -44,10 +44,11 @@ from .attention import (
     attend,
     swa_prefill,
     swa_decode,
+    swa_prefill_cached,
     swa_longformer,
     dense_masked_attention,
 )
-from .ring import ring_write, ring_from_sequence
+from .ring import ring_write, ring_append, ring_from_sequence
 from .tiles import band_tiles_bruteforce
 
 __all__ = [

@@ -101,6 +101,33 @@ def swa_decode(q, k_cache, v_cache, slot_pos, cur_pos, W, scale=None):
     return o, lse
 
 
+def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None):
+    """A chunk of L query tokens per request over a ring cache of S slots.
+
+    [G3] "How it works": queries carry absolute positions ([B, L]) and the cache
+    carries the position of each slot ([B, S]); the window is computed from
+    those positions, so query t attends the slots holding a position p with
+    q_pos[t]-W < p <= q_pos[t] (``decode_index_set`` with cur = q_pos[t]).  A
+    single-token chunk is ring decode.
+    q: [B, L, H_q, d_h]; k_cache, v_cache: [B, H_kv, S, d_h]; slot_pos: [B, S]
+    (< 0 = empty); q_pos: [B, L].  Returns o [B, L, H_q, d_h], lse [B, H_q, L].
+    """
+    B, L, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    group = Hq // Hkv
+    sc = _default_scale(D, scale)
+    o = np.zeros((B, L, Hq, v_cache.shape[-1]), dtype=np.float64)
+    lse = np.zeros((B, Hq, L), dtype=np.float64)
+    for b in range(B):
+        for t in range(L):
+            S_t = decode_index_set(slot_pos[b], int(q_pos[b, t]), W)
+            for h in range(Hq):
+                kvh = h // group
+                o[b, t, h], lse[b, h, t] = attend(q[b, t, h], k_cache[b, kvh, S_t],
+                                                  v_cache[b, kvh, S_t], sc)
+    return o, lse
+
+
 def swa_longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, rows=None, heads=None):
     """Longformer-style bidirectional attention: per-head dilated window + globals.
 

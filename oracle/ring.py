@@ -42,3 +42,18 @@ def ring_from_sequence(k_seq, v_seq, upto, W):
             v_cache[b, :, j] = v_seq[b, p]
             slot_pos[b, j] = p
     return k_cache, v_cache, slot_pos
+
+
+def ring_append(k_cache, v_cache, slot_pos, k_new, v_new, pos):
+    """Write a chunk of tokens per request into a ring of S slots, in place.
+
+    The same rule as ``ring_write`` applied to each token in order: token t of
+    request b lands in slot pos[b, t] mod S ([KB] §2 "KV cache") and the slot
+    records pos[b, t] ([G3] "How it works").
+    k_cache, v_cache: [B, H_kv, S, d]; slot_pos: [B, S];
+    k_new, v_new: [B, L, H_kv, d]; pos: [B, L] absolute positions.
+    """
+    B, L = np.asarray(pos).shape
+    for t in range(L):
+        ring_write(k_cache, v_cache, slot_pos, k_new[:, t], v_new[:, t], np.asarray(pos)[:, t])
+

@@ -298,6 +298,96 @@ def test_decode_ignores_slot_order_and_masks_stale_future_empty():
     assert np.all(o3 == 0) and np.all(np.isneginf(l3))
 
 
+# ---------------------------------------------------------------- chunked prefill over a ring
+
+def test_ring_append_is_ordered_token_writes_and_keeps_latest():
+    B, Hkv, D, S = 2, 2, 3, 7
+    rng = np.random.default_rng(40)
+    kc = np.zeros((B, Hkv, S, D)); vc = np.zeros_like(kc); sp = np.full((B, S), -1)
+    kc2, vc2, sp2 = kc.copy(), vc.copy(), sp.copy()
+    P = 0
+    for L in (3, 5, 1, 7, 4):                      # chunks of consecutive positions
+        pos = np.tile(np.arange(P, P + L), (B, 1))
+        kn, vn = rng.standard_normal((B, L, Hkv, D)), rng.standard_normal((B, L, Hkv, D))
+        oracle.ring_append(kc, vc, sp, kn, vn, pos)
+        for t in range(L):
+            oracle.ring_write(kc2, vc2, sp2, kn[:, t], vn[:, t], pos[:, t])
+        P += L
+    np.testing.assert_array_equal(kc, kc2)
+    np.testing.assert_array_equal(sp, sp2)
+    # slot j holds the latest position congruent to j (mod S)
+    for j in range(S):
+        assert sp[0, j] == max(p for p in range(P) if p % S == j)
+
+
+@pytest.mark.parametrize("W,L,p0", [(8, 5, 20), (16, 16, 40), (5, 12, 3), (30, 1, 25)])
+def test_prefill_cached_equals_prefill_rows(W, L, p0):
+    # a ring of S = W + L - 1 slots holding tokens 0 .. p0+L-1 (appended chunk by
+    # chunk, the last chunk being the queries' own tokens) gives prefill rows
+    # p0 .. p0+L-1
+    B, T, Hq, Hkv, D = 2, p0 + L, 4, 2, 8
+    q, k, v = _rand((B, T, Hq, D), 41), _rand((B, T, Hkv, D), 42), _rand((B, T, Hkv, D), 43)
+    S = W + L - 1
+    kc = np.zeros((B, Hkv, S, D)); vc = np.zeros_like(kc); sp = np.full((B, S), -1)
+    cuts = list(range(0, p0, 7)) + [p0, T]
+    for a, b_ in zip(cuts[:-1], cuts[1:]):
+        pos = np.tile(np.arange(a, b_), (B, 1))
+        oracle.ring_append(kc, vc, sp, k[:, a:b_], v[:, a:b_], pos)
+    qpos = np.tile(np.arange(p0, T), (B, 1))
+    o, lse = oracle.swa_prefill_cached(q[:, p0:T], kc, vc, sp, qpos, W)
+    op, lp = oracle.swa_prefill(q, k, v, W, rows=list(range(p0, T)))
+    np.testing.assert_allclose(o, op, atol=1e-12)
+    np.testing.assert_allclose(lse, lp, atol=1e-12)
+
+
+def test_prefill_cached_single_token_is_decode():
+    B, Hq, Hkv, D, S, W = 3, 4, 2, 8, 12, 9
+    rng = np.random.default_rng(44)
+    q = rng.standard_normal((B, 1, Hq, D))
+    kc, vc = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    sp = rng.integers(-3, 30, size=(B, S))
+    cur = np.array([10, 25, 2])
+    o, lse = oracle.swa_prefill_cached(q, kc, vc, sp, cur[:, None], W)
+    od, ld = oracle.swa_decode(q[:, 0], kc, vc, sp, cur, W)
+    np.testing.assert_allclose(o[:, 0], od, atol=1e-14)
+    np.testing.assert_allclose(lse[:, :, 0], ld, atol=1e-14)
+
+
+def test_prefill_cached_matches_position_mask_formula():
+    # [G3] "How it works": mask from absolute positions, 1[s > t-W] 1[s < t+W]
+    # times the causal factor 1[s <= t]; empty slots masked.  Checked against
+    # torch SDPA in float64 with that boolean mask, on a ring too small for the
+    # chunk (early queries have lost keys) and with stale / future / empty slots.
+    B, L, Hq, Hkv, D, S, W = 2, 6, 2, 1, 8, 9, 7
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((B, L, Hq, D))
+    kc, vc = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    sp = np.array([[13, 14, 15, 16, 17, 9, 10, 11, -1], [3, 30, 5, 6, -1, 8, 9, 1, 2]])
+    qpos = np.array([[12, 13, 14, 15, 16, 17], [4, 5, 6, 7, 8, 9]])
+    o, _ = oracle.swa_prefill_cached(q, kc, vc, sp, qpos, W)
+    for b in range(B):
+        t = qpos[b][:, None]
+        s_ = sp[b][None, :]
+        mask = (s_ > t - W) & (s_ < t + W) & (s_ <= t) & (s_ >= 0)
+        for h in range(Hq):
+            ref = _sdpa(q[b:b + 1, :, h:h + 1], kc[b, 0][None, :, None], vc[b, 0][None, :, None],
+                        False, mask=torch.from_numpy(mask))
+            np.testing.assert_allclose(o[b, :, h], ref[0, :, 0], atol=1e-12)
+
+
+def test_prefill_cached_ignores_slot_order():
+    B, L, Hq, Hkv, D, S, W = 1, 4, 2, 1, 4, 10, 6
+    rng = np.random.default_rng(46)
+    q = rng.standard_normal((B, L, Hq, D))
+    kc, vc = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    sp = rng.permutation(np.arange(S))[None] + 3
+    qpos = np.array([[7, 8, 9, 12]])
+    o, _ = oracle.swa_prefill_cached(q, kc, vc, sp, qpos, W)
+    perm = rng.permutation(S)
+    o2, _ = oracle.swa_prefill_cached(q, kc[:, :, perm], vc[:, :, perm], sp[:, perm], qpos, W)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+
+
 # ---------------------------------------------------------------- tiles
 
 def test_tiles_hand_example():
