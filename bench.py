@@ -4,7 +4,8 @@ One JSON line on stdout.  The headline is causal prefill at T=16384,
 W=4096, H_q=32, H_kv=8, d_h=128, bf16 (band-TFLOP/s: 4*d_h FLOP per attended
 (query head, key) pair, masked tile work excluded).  The other workloads
 (causal prefill B=2 T=32768 W=1024 local-layer shape, ring decode B=64 W=4096,
-Longformer B=8 T=4096 r=256) are reported in "extra".
+Longformer B=8 T=4096 r=256, chunked prefill of 512-token chunks over a ring
+cache) are reported in "extra".
 
 Timing: inputs resident in HBM, W untimed warm-up launches, then K launches
 bracketed by torch.cuda.synchronize() and HIP events recorded on the stream the
@@ -12,7 +13,7 @@ kernels are launched on (torch's current stream, which the binding passes to
 the library).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only prefill] [--profile-copy]
+                       [--only prefill|local|decode|longformer|chunk] [--profile-copy]
 """
 
 import argparse
@@ -139,6 +140,23 @@ def bench_longformer(c, steps, warmup):
                 frac_of_roof=t_roof / (ms * 1e-3))
 
 
+def bench_chunk(c, steps, warmup):
+    q, kc, vc, sp, qp = inp.chunk_inputs(c)
+    # attended (query token, slot) pairs, counted from the positions
+    spn, qpn = sp.numpy().astype(np.int64), qp.numpy().astype(np.int64)
+    pairs = 0
+    for b in range(c.B):
+        s_ = spn[b][None, :]
+        t_ = qpn[b][:, None]
+        pairs += int(((s_ >= 0) & (s_ > t_ - c.W) & (s_ <= t_)).sum())
+    pairs *= c.Hq
+    q, kc, vc, sp, qp = q.cuda(), kc.cuda(), vc.cuda(), sp.cuda(), qp.cuda()
+    o = torch.empty_like(q)
+    ms, _ = time_launches(lambda: bd.prefill_cached(q, kc, vc, sp, qp, c.W, out=o), steps, warmup)
+    flops = 4.0 * c.D * pairs
+    return dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12, pairs=pairs)
+
+
 def cpu_baseline(c, budget_s=12.0):
     """The fp64 oracle as it is, single-threaded, on steady-state rows of the
     headline workload, all heads; scaled to band-TFLOP/s."""
@@ -169,7 +187,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "longformer", "local"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "longformer", "local", "chunk"],
                     default="all", help="restrict to one workload (the headline always runs "
                     "unless decode/longformer/local is chosen)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -214,6 +232,15 @@ def main():
             value=round(r5["tflops"], 2), unit="TFLOP/s", ms=round(r5["ms"], 4),
             frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"],
             traffic_local_pass=measured_traffic("fwd_kernel<64, true, 4>@786432"))
+
+    if args.only in ("all", "chunk"):
+        c6 = inp.C6
+        r6 = bench_chunk(c6, max(20, args.steps), args.warmup)
+        extra["chunked_prefill"] = dict(
+            workload=f"chunked prefill over a ring cache B={c6.B} L={c6.L} S={c6.S} W={c6.W} "
+                     f"Hq={c6.Hq} Hkv={c6.Hkv} d_h={c6.D} bf16, chunk start in [{c6.p_lo}, {c6.p_hi})",
+            value=round(r6["tflops"], 2), unit="TFLOP/s", ms=round(r6["ms"], 4),
+            frac_mfma_peak=round(r6["tflops"] / PEAK_BF16_TFLOPS, 4), pairs=r6["pairs"])
 
     if main_r is None:
         print(json.dumps({"partial": args.only, "extra": extra}), flush=True)

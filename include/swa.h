@@ -14,6 +14,10 @@
  *                   Gemma 3" study note, "How it works")
  *   swa_longformer  symmetric window |i-j| <= r with per-head dilation and
  *                   global tokens (prathamp.com §1.1, §3.1, §4.3)
+ *   swa_prefill_cached  a chunk of queries with absolute positions over a ring
+ *                   cache of S slots (Gemma 3 note, "How it works": positions
+ *                   [B, L] against cache positions [B, S]); swa_decode is the
+ *                   one-token case
  *
  * Conventions shared by every entry point.
  *   - Tensors are caller-owned, contiguous, row-major DEVICE buffers unless an
@@ -100,6 +104,43 @@ swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const vo
 swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new,
                            const int32_t *pos, void *k_cache, void *v_cache, int32_t *slot_pos,
                            int B, int W, int H_kv, int d_h, void *stream);
+
+/* Ring-cache append of a chunk: token t of request b (k_new[b][t], v_new[b][t])
+ * goes to slot pos[b][t] mod S, which records slot_pos[b][slot] = pos[b][t]
+ * (knowledge base §2 "KV cache"; Gemma 3 note, "How it works").  The same rule
+ * as swa_cache_write applied to each token; a ring of S >= W + L - 1 slots
+ * keeps every key the chunk's own queries need after the append.
+ *   k_new, v_new     : [B, L, H_kv, d_h]      pos : [B, L] int32 (device)
+ *   k_cache, v_cache : [B, H_kv, S, d_h]      slot_pos : [B, S] int32
+ * Preconditions (device data, not checked): pos >= 0 (negative tokens are
+ * skipped) and the chunk's slots pos[b][t] mod S are distinct within each
+ * request (true for consecutive positions with L <= S); otherwise which token
+ * a shared slot keeps is unspecified.
+ * Errors: INVALID for null pointers, B, L, S, H_kv < 1, L > S, B, L or H_kv >
+ * 65535; UNSUPPORTED for other d_h. */
+swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
+                            const int32_t *pos, void *k_cache, void *v_cache, int32_t *slot_pos,
+                            int B, int L, int S, int H_kv, int d_h, void *stream);
+
+/* Chunked prefill over a ring cache (multi-token decode).  Query token t of
+ * request b has absolute position q_pos[b][t] and attends the slots j with
+ * slot_pos[b][j] >= 0 and q_pos[b][t]-W < slot_pos[b][j] <= q_pos[b][t]: the
+ * window is computed from the positions stored with the cache (Gemma 3 note,
+ * "How it works": M = 1[s > t-W] 1[s < t+W] with the causal s <= t), so slot
+ * order, stale, future and empty slots do not matter.  Write the chunk's own
+ * keys first (swa_cache_append) to let its queries see each other causally.
+ * A query with no valid slot gets o = 0 and lse = -inf.
+ *   q, o             : [B, L, H_q, d_h]
+ *   k_cache, v_cache : [B, H_kv, S, d_h]
+ *   slot_pos         : [B, S] int32     q_pos : [B, L] int32, >= 0  (device)
+ *   lse              : [B, H_q, L] float32 or NULL
+ * No workspace.  Errors: INVALID for null pointers, B, L, S, H_q, H_kv < 1,
+ * W < 1, H_q % H_kv != 0, bad scale; UNSUPPORTED for other d_h or (bf16) a
+ * per-head cache slice of 2 GiB or more. */
+swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *slot_pos, const int32_t *q_pos,
+                              void *o, float *lse, int B, int L, int S, int H_q, int H_kv,
+                              int d_h, int W, float scale, void *stream);
 
 /* Longformer-style bidirectional attention.
  * A non-global row i of head h attends {i + k*dil[h] : -r <= k <= r} inside

@@ -22,13 +22,19 @@
 // K operand reads and the transposing V reads hit distinct LDS banks.
 //
 // The score definition is the masked softmax of [KB] §2 (alpha^SWA, o^SWA);
-// windows: causal t-W < s <= t ([KB] §2-§3), or, in symmetric mode, the
+// windows: causal t-W < s <= t ([KB] §2-§3); in symmetric mode, the
 // undilated window |i-j| <= r inside one residue class of a dilated head plus
-// the global keys not already in the window ([PP] §1.1, §3.1, §4.3).
+// the global keys not already in the window ([PP] §1.1, §3.1, §4.3); in ring
+// mode, a chunk of queries with absolute positions against the slots of a ring
+// cache, slot attended iff its stored position p has q_pos-W < p <= q_pos
+// ([G3] "How it works": the window comes from positions, not buffer offsets).
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [PP] "Sliding Window Attention: From Local Windows to Global Context"
-// (prathamp.com); [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai).
+// (prathamp.com); [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai);
+// [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive.pages.dev).
+
+#include <climits>
 
 #include "swa_internal.h"
 
@@ -150,6 +156,19 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
   }
 }
 
+// One 4-byte copy per lane (global_load_lds_dword): lane i's word lands at LDS
+// byte m0 + 4*i.
+__device__ inline void dma_dword(const char *gbase, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %3, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "s"(uni_ptr(gbase)), "v"(off));
+}
+
 // Wait until at most n of this wave's vector-memory operations are still in
 // flight (they complete in issue order), i.e. every copy except the n most
 // recent has landed in LDS.  Inline assembly: the compiler does not know about
@@ -188,14 +207,19 @@ struct IntC {
 constexpr float kLazy = 8.f;
 
 // NW waves per workgroup; three waves per SIMD (12 per CU) bound the registers.
-template <int D, bool SYM, int NW>
+// MODE: kCausal, kSymmetric or kRing (FwdMode).
+template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
     const FwdArgs a, const GlobalList gl) {
+  constexpr bool SYM = MODE == kSymmetric;
+  constexpr bool RING = MODE == kRing;
   using Gm = Geo<D>;
   // NST stages, each a row-major K tile followed by a V tile (swizzled
   // chunks); copies run NST-1 tiles ahead of the compute.  After the loop the
   // same memory stages the output rows.
-  constexpr int STAGE_B = 2 * Gm::TILE_B;
+  // ring mode: the tile's slot positions follow its V tile (256 bytes)
+  constexpr int SP_OFF = 2 * Gm::TILE_B;
+  constexpr int STAGE_B = 2 * Gm::TILE_B + (RING ? 256 : 0);
   constexpr int NST = 2;
   constexpr int OST_B = NW * kRowsPerWave * D * 2;
   constexpr int SMEM_B = (NST * STAGE_B > OST_B) ? NST * STAGE_B : OST_B;
@@ -264,8 +288,9 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   const long long q_rowstride = a.q_st * dil;
   const long long k_rowstride = a.k_st * dil;
   const long long k_rho = (long long)rho * a.k_st;
-  const uint16_t *kbase = kg + (long long)b * a.k_sb + (long long)kvh * D;
-  const uint16_t *vbase = vg + (long long)b * a.k_sb + (long long)kvh * D;
+  const uint16_t *kbase = kg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
+  const uint16_t *vbase = vg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
+  const int n_keyrows = RING ? a.S : n_cls;  // key rows of this (batch, head)
 
   // -------- Q (B operand of S^T = K Q^T): lane holds row lq, columns 16ks + 8lh .. +7
   bf16x8 qf[KS_QK];
@@ -288,7 +313,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
 
   // -------- schedule
   TileRange tr;
-  if constexpr (!SYM) tr = causal_tile_range(tile_row0, t1_valid, a.W, BN);
+  if constexpr (RING) tr = {0, ceil_div(a.S, BN) - 1};  // every slot tile
+  else if constexpr (!SYM) tr = causal_tile_range(tile_row0, t1_valid, a.W, BN);
   else tr = sym_tile_range(tile_row0, t1_valid, a.W, n_cls, BN);
   tr.lo = uni(tr.lo);
   tr.hi = uni(tr.hi);
@@ -299,7 +325,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   const int w_last = min(row0 + kRowsPerWave, n_cls) - 1;
   TileRange wr{1, 0};
   if (w_last >= row0) {
-    if constexpr (!SYM) wr = causal_tile_range(row0, w_last, a.W, BN);
+    if constexpr (RING) wr = tr;
+    else if constexpr (!SYM) wr = causal_tile_range(row0, w_last, a.W, BN);
     else wr = sym_tile_range(row0, w_last, a.W, n_cls, BN);
   }
   wr.lo = uni(wr.lo);
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   // DMA of the K and V rows of tile j (window tiles j < n_win, then tiles of
   // global keys) into the stage at LDS address `stage`.
   auto issue = [&](int j, uint32_t stage) {
-    const bool whole = j < n_win && (tr.lo + j) * BN + BN <= n_cls;
+    const bool whole = j < n_win && (tr.lo + j) * BN + BN <= n_keyrows;
     const long long base = (k_rho + (long long)(tr.lo + j) * BN * k_rowstride) * 2;
 #pragma unroll
     for (int t = 0; t < NSLOT; ++t) {
@@ -347,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           const int p = lane % Gm::CPR;
           long long o;
           if (j < n_win) {
-            const int sr = min((tr.lo + j) * BN + r, n_cls - 1);
+            const int sr = min((tr.lo + j) * BN + r, n_keyrows - 1);
             o = (k_rho + (long long)sr * k_rowstride) * 2;
           } else {
             const int u = min((j - n_win) * BN + r, a.G - 1);
@@ -356,6 +383,15 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           const uint32_t off = (uint32_t)o + (p ^ (isv ? swz_v<D>(r) : swz_k<D>(r))) * 16;
           dma_tile<1>(g8, &off, ld);
         }
+      }
+    }
+    if constexpr (RING) {
+      // the tile's slot positions (lane i: slot tile*BN + i, clamped; the
+      // mask ignores slots past S)
+      if (wave == NW - 1) {
+        const int slot = min((tr.lo + j) * BN + lane, a.S - 1);
+        dma_dword(reinterpret_cast<const char *>(a.slot_pos + (long long)b * a.S),
+                  (uint32_t)slot * 4u, stage + (uint32_t)SP_OFF);
       }
     }
   };
@@ -472,6 +508,55 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     if constexpr (!SYM) return causal_tile_full(row0, w_last, kj, BN, a.W, n_cls);
     else return sym_tile_full(row0, w_last, kj, BN, a.W, n_cls);
   };
+  // Ring mode: this lane's query position and the wave's position range.
+  int my_pos = 0, pos_lo = 0, pos_hi = 0;
+  if constexpr (RING) {
+    const bool ok = my_row < n_cls;
+    my_pos = ok ? a.q_pos[(long long)b * a.T + my_row] : 0;
+    int lo = ok ? my_pos : INT_MAX, hi = ok ? my_pos : INT_MIN;
+#pragma unroll
+    for (int x = 16; x >= 1; x >>= 1) {
+      lo = min(lo, __shfl_xor(lo, x));
+      hi = max(hi, __shfl_xor(hi, x));
+    }
+    pos_lo = uni(lo);
+    pos_hi = uni(hi);
+    asm volatile("" ::"v"(my_pos));
+  }
+  // Ring tile with every (valid row, slot) pair attended: all slots exist,
+  // are filled and lie in the window of every row of the wave.
+  auto ring_full = [&](const char *stg, int j) {
+    const int n_in = min(BN, a.S - (tr.lo + j) * BN);
+    const int sp = reinterpret_cast<const int *>(stg + SP_OFF)[lane % BN];
+    int lo = sp, hi = sp;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) {
+      lo = min(lo, __shfl_xor(lo, x));
+      hi = max(hi, __shfl_xor(hi, x));
+    }
+    return n_in == BN && uni(lo) >= 0 && (long long)uni(lo) > (long long)pos_hi - a.W &&
+           uni(hi) <= pos_lo;
+  };
+  // Ring mask: slot k of the tile (k < S) is attended iff its position p has
+  // p >= 0 and my_pos - W < p <= my_pos.
+  auto ring_mask = [&](const char *stg, int j, f32x16 *sv) {
+    const int n_in = min(BN, a.S - (tr.lo + j) * BN);
+    const int *spl = reinterpret_cast<const int *>(stg + SP_OFF);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int k0 = kb * 32 + 8 * g4 + 4 * lh;
+        const int4 p4 = *reinterpret_cast<const int4 *>(spl + k0);
+        const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = pv[i];
+          const bool ok = k0 + i < n_in && p >= 0 && p > my_pos - a.W && p <= my_pos;
+          if (!ok) sv[kb][4 * g4 + i] = -INFINITY;
+        }
+      }
+  };
   // Attended keys of row my_row inside the window, [lo_key, hi_key]: the
   // causal predicate (t-W < s <= t) or the symmetric one (|i-j| <= r), cut at
   // the class length.
@@ -535,7 +620,11 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       f32x16 sv[KB];
       U4 pu[PK];
       qk(ks, sv);
-      if (!tile_full(j)) mask(j, sv);
+      if constexpr (RING) {
+        if (!ring_full(ks, j)) ring_mask(ks, j, sv);
+      } else {
+        if (!tile_full(j)) mask(j, sv);
+      }
       rescale(rowmax(sv));
       exp_pack(sv, pu);
       pv(ks + Gm::TILE_B, pu);
@@ -599,19 +688,22 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st) {
-  const int nblk = symmetric ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
+  const int nblk = mode == kSymmetric ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
   if (nblk <= 0) return hipSuccess;
   constexpr int NWC = SWA_FWD_WAVES;
-  if (a.NW != (symmetric ? 4 : NWC)) return hipErrorInvalidValue;
+  if (a.NW != (mode == kSymmetric ? 4 : NWC)) return hipErrorInvalidValue;
   dim3 grid(nblk), block(64 * a.NW);
-  if (!symmetric) {
-    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, false, NWC>), grid, block, 0, st, a, *gl);
-    else hipLaunchKernelGGL((fwd_kernel<64, false, NWC>), grid, block, 0, st, a, *gl);
+  if (mode == kCausal) {
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausal, NWC>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, kCausal, NWC>), grid, block, 0, st, a, *gl);
+  } else if (mode == kRing) {
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kRing, NWC>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, kRing, NWC>), grid, block, 0, st, a, *gl);
   } else {
-    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, true, 4>), grid, block, 0, st, a, *gl);
-    else hipLaunchKernelGGL((fwd_kernel<64, true, 4>), grid, block, 0, st, a, *gl);
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kSymmetric, 4>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, kSymmetric, 4>), grid, block, 0, st, a, *gl);
   }
   return hipGetLastError();
 }

@@ -9,18 +9,23 @@
 // Connectivity sets: causal t-W < s <= t ([KB] §2-§3); Longformer: a global
 // row attends every position, any other row attends i + k*dil (|k| <= r) inside
 // [0, T) plus the global positions not already in that window ([PP] §1.1,
-// §3.1, §4.3).  Scores use the masked softmax of [KB] §2.
+// §3.1, §4.3); ring: a query at absolute position p attends the ring slots
+// holding a position in (p-W, p] ([G3] "How it works").  Scores use the
+// masked softmax of [KB] §2.
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
-// [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com).
+// [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com);
+// [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive.pages.dev).
 
 #include "swa_internal.h"
 
 namespace swa {
 namespace {
 
-template <int D, bool SYM>
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const GlobalList gl) {
+  constexpr bool SYM = MODE == kSymmetric;
+  constexpr bool RING = MODE == kRing;
   constexpr int DPL = D / 64;  // output columns per lane
   __shared__ float qs[4][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -32,8 +37,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   const int b = live ? (int)(row_id / ((long long)a.T * a.Hq)) : 0;
   const int kvh = SYM ? h : h / a.group;
   const float *q = static_cast<const float *>(a.q);
-  const float *k = static_cast<const float *>(a.k) + (long long)b * a.k_sb + (long long)kvh * D;
-  const float *v = static_cast<const float *>(a.v) + (long long)b * a.k_sb + (long long)kvh * D;
+  const float *k = static_cast<const float *>(a.k) + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
+  const float *v = static_cast<const float *>(a.v) + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   for (int d = lane; d < D; d += 64)
     qs[wave][d] = live ? q[(long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D + d] : 0.f;
   __syncthreads();
@@ -43,7 +48,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   int n_keys, base = 0, kstep = 1, n_win = 0;
   bool is_glob = false;
   const int dil = SYM ? a.dil[h] : 1;
-  if constexpr (!SYM) {
+  int my_pos = 0;
+  if constexpr (RING) {
+    n_keys = a.S;  // every slot; the position test below picks the window
+    my_pos = a.q_pos[(long long)b * a.T + t];
+  } else if constexpr (!SYM) {
     base = max(0, t - a.W + 1);
     n_keys = t - base + 1;
   } else {
@@ -68,7 +77,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
     const int idx = c0 + lane;
     int key = -1;
     if (idx < n_keys) {
-      if (!SYM || is_glob) key = base + idx * kstep;
+      if constexpr (RING) {
+        const int p = a.slot_pos[(long long)b * a.S + idx];
+        key = (p >= 0 && p > my_pos - a.W && p <= my_pos) ? idx : -1;
+      } else if (!SYM || is_glob) key = base + idx * kstep;
       else if (idx < n_win) key = base + idx * kstep;
       else {
         const int g = gl.idx[b * a.G + idx - n_win];
@@ -118,17 +130,21 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                           hipStream_t st) {
   const long long rows = (long long)a.B * a.Hq * a.T;
   const int blocks = (int)((rows + 3) / 4);
   if (blocks <= 0) return hipSuccess;
-  if (!symmetric) {
-    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, false>), dim3(blocks), dim3(256), 0, st, a, *gl);
-    else hipLaunchKernelGGL((fwd_f32_kernel<64, false>), dim3(blocks), dim3(256), 0, st, a, *gl);
+  const dim3 g(blocks), blk(256);
+  if (mode == kCausal) {
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kCausal>), g, blk, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, kCausal>), g, blk, 0, st, a, *gl);
+  } else if (mode == kRing) {
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kRing>), g, blk, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, kRing>), g, blk, 0, st, a, *gl);
   } else {
-    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, true>), dim3(blocks), dim3(256), 0, st, a, *gl);
-    else hipLaunchKernelGGL((fwd_f32_kernel<64, true>), dim3(blocks), dim3(256), 0, st, a, *gl);
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kSymmetric>), g, blk, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, kSymmetric>), g, blk, 0, st, a, *gl);
   }
   return hipGetLastError();
 }

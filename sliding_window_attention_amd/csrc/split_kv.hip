@@ -534,19 +534,23 @@ hipError_t run(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) 
   return hipGetLastError();
 }
 
+// Ring append ([KB] §2 "KV cache": token i lives in slot i mod S; the slot
+// records its absolute position, [G3] "How it works").  Block (hk, t, b) copies
+// token t's key and value rows of head hk; the chunk's slots are distinct (a
+// documented precondition), so blocks never write the same slot.
 __global__ void cache_write_kernel(const char *kn, const char *vn, const int *pos, char *kc,
-                                   char *vc, int *slot_pos, int W, int Hkv, int row_bytes) {
-  const int b = blockIdx.y, hk = blockIdx.x;
-  const int p = pos[b];
+                                   char *vc, int *slot_pos, int L, int S, int Hkv, int row_bytes) {
+  const int hk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int p = pos[(long long)b * L + t];
   if (p < 0) return;  // documented precondition; never index with a negative slot
-  const int slot = p % W;
-  const long long src = ((long long)b * Hkv + hk) * row_bytes;
-  const long long dst = (((long long)b * Hkv + hk) * W + slot) * row_bytes;
+  const int slot = p % S;
+  const long long src = (((long long)b * L + t) * Hkv + hk) * row_bytes;
+  const long long dst = (((long long)b * Hkv + hk) * S + slot) * row_bytes;
   for (int i = threadIdx.x * 4; i < row_bytes; i += blockDim.x * 4) {
     *reinterpret_cast<uint32_t *>(kc + dst + i) = *reinterpret_cast<const uint32_t *>(kn + src + i);
     *reinterpret_cast<uint32_t *>(vc + dst + i) = *reinterpret_cast<const uint32_t *>(vn + src + i);
   }
-  if (hk == 0 && threadIdx.x == 0) slot_pos[(long long)b * W + slot] = p;
+  if (hk == 0 && threadIdx.x == 0) slot_pos[(long long)b * S + slot] = p;
 }
 
 __global__ void debug_mask_kernel(int mode, int T, int w_or_r, int dil, const GlobalList gl, int G,
@@ -584,12 +588,13 @@ hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const 
 int split_max_chunk() { return kMaxChunk; }
 
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
-                              void *vc, int *slot_pos, int B, int W, int Hkv, int D,
+                              void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,
                               hipStream_t st) {
   const int row_bytes = D * (f32 ? 4 : 2);
-  hipLaunchKernelGGL(cache_write_kernel, dim3(Hkv, B), dim3(64), 0, st,
+  hipLaunchKernelGGL(cache_write_kernel, dim3(Hkv, L, B), dim3(64), 0, st,
                      static_cast<const char *>(kn), static_cast<const char *>(vn), pos,
-                     static_cast<char *>(kc), static_cast<char *>(vc), slot_pos, W, Hkv, row_bytes);
+                     static_cast<char *>(kc), static_cast<char *>(vc), slot_pos, L, S, Hkv,
+                     row_bytes);
   return hipGetLastError();
 }
 

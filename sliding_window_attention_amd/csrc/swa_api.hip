@@ -141,6 +141,7 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
   a.q_sb = a.q_st * T;
   a.k_st = (long long)H_kv * d_h;
   a.k_sb = a.k_st * T;
+  a.k_sh = d_h;
   a.W = W;
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
@@ -152,11 +153,54 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, false, d_h, &gl, st));
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, kCausal, d_h, &gl, st));
   // bf16 kernels address one batch slice of K/V with 32-bit byte offsets
   if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31))
     return SWA_ERR_UNSUPPORTED;
-  return hip_status(launch_fwd_bf16(a, false, d_h, &gl, st));
+  return hip_status(launch_fwd_bf16(a, kCausal, d_h, &gl, st));
+}
+
+swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *slot_pos, const int32_t *q_pos,
+                              void *o, float *lse, int B, int L, int S, int H_q, int H_kv,
+                              int d_h, int W, float scale, void *stream) {
+  if (!dt_ok(dt) || !q || !k_cache || !v_cache || !slot_pos || !q_pos || !o)
+    return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(slot_pos, 4) || !aligned(q_pos, 4) || (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || L < 1 || S < 1 || H_q < 1 || H_kv < 1 || W < 1 || H_q % H_kv || !scale_ok(scale))
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.B = B; a.T = L; a.Hq = H_q; a.Hkv = H_kv;
+  a.q_st = (long long)H_q * d_h;
+  a.q_sb = a.q_st * L;
+  a.k_st = d_h;                        // [B, H_kv, S, d_h]: rows of one head are contiguous
+  a.k_sh = (long long)S * d_h;
+  a.k_sb = a.k_sh * H_kv;
+  a.W = W;
+  a.sl2 = scale * kLog2e;
+  a.group = H_q / H_kv;
+  a.P = prefill_pack(H_q, H_kv);
+  a.NW = fwd_waves(false);
+  a.BM = kRowsPerWave * a.NW / a.P;
+  a.n_qt = (L + a.BM - 1) / a.BM;
+  a.n_hg = H_q / a.P;
+  a.slot_pos = slot_pos;
+  a.q_pos = q_pos;
+  a.S = S;
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, kRing, d_h, &gl, st));
+  // bf16 kernels address one (batch, head) slice of K/V with 32-bit byte offsets
+  if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL || a.k_sh * 2 >= (1LL << 31))
+    return SWA_ERR_UNSUPPORTED;
+  return hip_status(launch_fwd_bf16(a, kRing, d_h, &gl, st));
 }
 
 size_t swa_decode_workspace_size(int B, int H_q, int H_kv, int W, int d_h) {
@@ -209,10 +253,26 @@ swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new, c
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(pos, 4) || !aligned(slot_pos, 4))
     return SWA_ERR_INVALID;
-  if (B < 1 || W < 1 || H_kv < 1) return SWA_ERR_INVALID;
+  if (B < 1 || W < 1 || H_kv < 1 || B > 65535) return SWA_ERR_INVALID;
   if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
   return hip_status(launch_cache_write(dt == SWA_F32, k_new, v_new, pos, k_cache, v_cache,
-                                       slot_pos, B, W, H_kv, d_h,
+                                       slot_pos, B, 1, W, H_kv, d_h,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
+                            const int32_t *pos, void *k_cache, void *v_cache, int32_t *slot_pos,
+                            int B, int L, int S, int H_kv, int d_h, void *stream) {
+  if (!dt_ok(dt) || !k_new || !v_new || !pos || !k_cache || !v_cache || !slot_pos)
+    return SWA_ERR_INVALID;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(pos, 4) || !aligned(slot_pos, 4))
+    return SWA_ERR_INVALID;
+  if (B < 1 || L < 1 || S < 1 || L > S || H_kv < 1 || L > 65535 || H_kv > 65535 || B > 65535)
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  return hip_status(launch_cache_write(dt == SWA_F32, k_new, v_new, pos, k_cache, v_cache,
+                                       slot_pos, B, L, S, H_kv, d_h,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -254,6 +314,7 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   a.q_sb = a.q_st * T;
   a.k_st = a.q_st;
   a.k_sb = a.q_sb;
+  a.k_sh = d_h;
   a.W = r;
   a.sl2 = scale * kLog2e;
   a.group = 1;
@@ -276,9 +337,9 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   std::memset(&gl, 0, sizeof(gl));
   for (int i = 0; i < B * G; ++i) gl.idx[i] = global_idx[i];
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, true, d_h, &gl, st));
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, kSymmetric, d_h, &gl, st));
 
-  hipError_t e = launch_fwd_bf16(a, true, d_h, &gl, st);
+  hipError_t e = launch_fwd_bf16(a, kSymmetric, d_h, &gl, st);
   if (e != hipSuccess || G == 0) return hip_status(e);
   // Global rows attend every position: split-KV over all T keys, written after
   // (stream order) the local pass, replacing those rows.

@@ -148,7 +148,8 @@ struct FwdArgs {
   float *lse;
   int B, T, Hq, Hkv;
   long long q_sb, q_st;  // element strides of q/o: batch, token (head stride = D)
-  long long k_sb, k_st;  // element strides of k/v
+  long long k_sb, k_st;  // element strides of k/v: batch, key row
+  long long k_sh;        // element stride of k/v heads (d_h for [B, T, H, d_h])
   int W;                 // causal window, or radius r in symmetric mode
   float sl2;             // scale * log2(e)
   int P, group;          // heads per workgroup, H_q / H_kv
@@ -160,7 +161,14 @@ struct FwdArgs {
   int tiles_per_batch;         // sum over heads of class tiles
   int head_off[kMaxHeadsLF + 1];   // prefix sums of class tiles per head
   unsigned short dil[kMaxHeadsLF]; // per-head dilation
+  // ring mode (a chunk of queries over a ring cache)
+  const int *slot_pos;   // [B, S] position held by each slot (< 0 = empty)
+  const int *q_pos;      // [B, T] absolute position of each query row
+  int S;                 // ring slots (key rows per batch and head)
 };
+
+// Window families of the banded kernels.
+enum FwdMode { kCausal = 0, kSymmetric = 1, kRing = 2 };
 
 struct GlobalList {
   int idx[kMaxGlobalsLF];  // [B][G] positions
@@ -185,14 +193,14 @@ struct SplitArgs {
 
 // ---------------------------------------------------------------- launchers (host)
 
-hipError_t launch_fwd_bf16(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st);
-hipError_t launch_fwd_f32(const FwdArgs &a, bool symmetric, int D, const GlobalList *gl,
+hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                           hipStream_t st);
 hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const GlobalList *gl,
                         int G, int H, hipStream_t st);
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
-                              void *vc, int *slot_pos, int B, int W, int Hkv, int D,
+                              void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,
                               hipStream_t st);
 hipError_t launch_debug_mask(int mode, int T, int w_or_r, int dil, const GlobalList *gl, int G,
                              uint8_t *mask, hipStream_t st);

@@ -92,13 +92,32 @@ class LongformerCase:
     seed: int = 0
 
 
-# The five workloads (shapes of the pages' examples; see the design doc for the recipe).
+@dataclass
+class ChunkCase:
+    B: int
+    L: int         # query tokens per request (the chunk)
+    S: int         # ring slots
+    W: int
+    Hq: int
+    Hkv: int
+    D: int
+    p_lo: int      # first chunk position ~ U[p_lo, p_hi)
+    p_hi: int
+    dtype: str = "bf16"
+    seed: int = 0
+
+
+# The workloads (shapes of the pages' examples; see the design doc for the recipe).
 C1 = LongformerCase(B=1, T=16, H=1, D=64, r=2, dilation=[1], globals_=[], dtype="f32", seed=1000)
 C2 = PrefillCase(B=1, T=16384, Hq=32, Hkv=8, D=128, W=4096, seed=1001)
 C3 = PrefillCase(B=2, T=32768, Hq=32, Hkv=16, D=128, W=1024, rope=True, seed=1002)
 C4 = DecodeCase(B=64, W=4096, Hq=32, Hkv=8, D=128, cur_lo=4096, cur_hi=32768, seed=1003)
 C5 = LongformerCase(B=8, T=4096, H=12, D=64, r=256, dilation=[1] * 8 + [2] * 4,
                     globals_=[0, 8], seed=1004)
+# chunked prefill into a Mistral-shaped ring: 512-token chunks, W = 4096, a ring
+# of W + L - 1 slots, chunk starts anywhere in a 32K context
+C6 = ChunkCase(B=4, L=512, S=4096 + 511, W=4096, Hq=32, Hkv=8, D=128, p_lo=4096,
+               p_hi=32768 - 512, seed=1006)
 
 
 def prefill_inputs(c: PrefillCase):
@@ -137,6 +156,25 @@ def decode_inputs(c: DecodeCase):
     slot_pos = full_ring_positions(cur, c.W)
     return (as_io(q, c.dtype), as_io(k, c.dtype), as_io(v, c.dtype),
             torch.from_numpy(slot_pos), torch.from_numpy(cur))
+
+
+def chunk_inputs(c: ChunkCase):
+    """q [B,L,Hq,D], k_cache, v_cache [B,Hkv,S,D], slot_pos [B,S] int32,
+    q_pos [B,L] int32.
+
+    The chunk of request b holds positions p0_b .. p0_b+L-1 with p0_b ~
+    U[p_lo, p_hi); the ring holds tokens 0 .. p0_b+L-1 (the chunk already
+    appended), i.e. slot j holds the newest such position congruent to j mod S.
+    """
+    rng = np.random.default_rng(c.seed)
+    q = rng.standard_normal((c.B, c.L, c.Hq, c.D), dtype=np.float32)
+    k = rng.standard_normal((c.B, c.Hkv, c.S, c.D), dtype=np.float32)
+    v = rng.standard_normal((c.B, c.Hkv, c.S, c.D), dtype=np.float32)
+    p0 = rng.integers(c.p_lo, c.p_hi, size=c.B).astype(np.int64)
+    q_pos = (p0[:, None] + np.arange(c.L)[None, :]).astype(np.int32)
+    slot_pos = full_ring_positions(p0 + c.L - 1, c.S)
+    return (as_io(q, c.dtype), as_io(k, c.dtype), as_io(v, c.dtype),
+            torch.from_numpy(slot_pos), torch.from_numpy(q_pos))
 
 
 def longformer_inputs(c: LongformerCase):

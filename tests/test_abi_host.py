@@ -119,6 +119,45 @@ def test_cache_write_and_debug_validation():
     assert L.swa_debug_index_mask(1, 16, 2, 1, g, 1, P, S0) == INVALID
 
 
+def _cached(**kw):
+    a = dict(dt=0, q=P, kc=P, vc=P, sp=P, qp=P, o=P, lse=None, B=2, L=5, S=40, Hq=4, Hkv=2,
+             D=128, W=16, sc=0.1)
+    a.update(kw)
+    return bd.lib().swa_prefill_cached(a["dt"], a["q"], a["kc"], a["vc"], a["sp"], a["qp"],
+                                       a["o"], a["lse"], a["B"], a["L"], a["S"], a["Hq"],
+                                       a["Hkv"], a["D"], a["W"], a["sc"], S0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(sp=None), INVALID), (dict(qp=None), INVALID),
+    (dict(qp=ctypes.c_void_p(4098)), INVALID), (dict(kc=ctypes.c_void_p(4104)), INVALID),
+    (dict(B=0), INVALID), (dict(L=0), INVALID), (dict(S=0), INVALID), (dict(W=0), INVALID),
+    (dict(Hq=5), INVALID), (dict(sc=-1.0), INVALID), (dict(dt=3), INVALID),
+    (dict(D=32), UNSUPPORTED),
+    (dict(dt=0, S=1 << 23, D=128), UNSUPPORTED),   # bf16 head slice of 2 GiB
+])
+def test_prefill_cached_validation(kw, code):
+    assert _cached(**kw) == code
+
+
+def test_cache_append_validation():
+    L = bd.lib()
+    ok = dict(dt=0, kn=P, vn=P, pos=P, kc=P, vc=P, sp=P, B=2, L=4, S=8, Hkv=2, D=64)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.swa_cache_append(a["dt"], a["kn"], a["vn"], a["pos"], a["kc"], a["vc"], a["sp"],
+                                  a["B"], a["L"], a["S"], a["Hkv"], a["D"], S0)
+
+    assert call(sp=None) == INVALID
+    assert call(kn=ctypes.c_void_p(4100)) == INVALID
+    assert call(L=0) == INVALID
+    assert call(L=9) == INVALID          # more tokens than slots
+    assert call(B=70000) == INVALID
+    assert call(D=100) == UNSUPPORTED
+
+
 def test_tile_config():
     # 4 waves of 32 rows; 4 (2, 1) query heads share a K/V tile
     assert bd.tile_config("p", 32, 8, 128) == (32, 32)
