@@ -34,6 +34,7 @@ beyond the special cases and invariants listed in the tests).
 
 from .index_sets import (
     causal_index_set,
+    causal_sink_index_set,
     symmetric_index_set,
     longformer_index_set,
     decode_index_set,
@@ -48,7 +49,7 @@ from .attention import (
     swa_longformer,
     dense_masked_attention,
 )
-from .ring import ring_write, ring_append, ring_from_sequence
+from .ring import ring_write, ring_slot, ring_append, ring_from_sequence
 from .tiles import band_tiles_bruteforce
 
 __all__ = [

@@ -21,28 +21,38 @@ import math
 
 import numpy as np
 
-from .index_sets import causal_index_set, decode_index_set, longformer_index_set
+from .index_sets import (causal_index_set, causal_sink_index_set, decode_index_set,
+                         longformer_index_set)
 
 
 def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def attend(q_row, K, V, scale):
+def attend(q_row, K, V, scale, sink_logit=None):
     """One query row over the key/value rows of its connectivity set.
 
     Returns (o [d_v], lse).  An empty set yields o = 0 and lse = -inf (a reading:
     the pages never produce an empty window; only an empty ring cache does).
+
+    ``sink_logit`` (a reading of the learned per-head sink of [ST] "What's New"):
+    a score z that joins the softmax denominator with no value row, i.e. an
+    always-visible virtual position whose value is zero:
+        o = sum_s exp(e_s) v_s / (exp(z) + sum_s exp(e_s)),
+        lse = log(exp(z) + sum_s exp(e_s)).
     """
     q_row = _f64(q_row)
     K = _f64(K)
     V = _f64(V)
+    z = None if sink_logit is None else float(sink_logit)
     if K.shape[0] == 0:
-        return np.zeros(V.shape[-1], dtype=np.float64), -math.inf
+        if z is None:
+            return np.zeros(V.shape[-1], dtype=np.float64), -math.inf
+        return np.zeros(V.shape[-1], dtype=np.float64), z
     e = (K @ q_row) * float(scale)            # scores over S_t
-    m = e.max()
+    m = e.max() if z is None else max(e.max(), z)
     p = np.exp(e - m)                        # weights before normalisation
-    l = p.sum()
+    l = p.sum() + (0.0 if z is None else math.exp(z - m))
     o = (p @ V) / l
     return o, m + math.log(l)
 
@@ -51,7 +61,7 @@ def _default_scale(d_h, scale):
     return 1.0 / math.sqrt(d_h) if scale is None else float(scale)
 
 
-def swa_prefill(q, k, v, W, scale=None, rows=None):
+def swa_prefill(q, k, v, W, scale=None, rows=None, n_sink=0, sink_logit=None):
     """Causal sliding-window prefill with grouped-query heads.
 
     q: [B, T, H_q, d_h]; k, v: [B, T, H_kv, d_h]; query head h reads key/value
@@ -59,6 +69,9 @@ def swa_prefill(q, k, v, W, scale=None, rows=None):
     fixes only that several query heads share one key/value head, the grouping
     is a reading).  S_t is the causal window of ``causal_index_set``.
     ``rows`` optionally restricts the computation to those query positions.
+    ``n_sink`` > 0 adds the first n_sink positions to every window
+    (``causal_sink_index_set``); ``sink_logit`` [H_q] gives each head a sink
+    score in the denominator (see ``attend``).
     Returns o [B, R, H_q, d_h] and lse [B, H_q, R] (R = len(rows) or T).
     """
     B, T, Hq, D = q.shape
@@ -72,10 +85,11 @@ def swa_prefill(q, k, v, W, scale=None, rows=None):
     lse = np.zeros((B, Hq, len(rows)), dtype=np.float64)
     for b in range(B):
         for ri, t in enumerate(rows):
-            S = causal_index_set(int(t), W)
+            S = causal_sink_index_set(int(t), W, n_sink) if n_sink else causal_index_set(int(t), W)
             for h in range(Hq):
                 kvh = h // group
-                o[b, ri, h], lse[b, h, ri] = attend(q[b, t, h], k[b, S, kvh], v[b, S, kvh], sc)
+                z = None if sink_logit is None else sink_logit[h]
+                o[b, ri, h], lse[b, h, ri] = attend(q[b, t, h], k[b, S, kvh], v[b, S, kvh], sc, z)
     return o, lse
 
 
@@ -101,14 +115,16 @@ def swa_decode(q, k_cache, v_cache, slot_pos, cur_pos, W, scale=None):
     return o, lse
 
 
-def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None):
+def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None, n_sink=0,
+                       sink_logit=None):
     """A chunk of L query tokens per request over a ring cache of S slots.
 
     [G3] "How it works": queries carry absolute positions ([B, L]) and the cache
     carries the position of each slot ([B, S]); the window is computed from
     those positions, so query t attends the slots holding a position p with
     q_pos[t]-W < p <= q_pos[t] (``decode_index_set`` with cur = q_pos[t]).  A
-    single-token chunk is ring decode.
+    single-token chunk is ring decode.  ``n_sink`` / ``sink_logit`` as in
+    ``swa_prefill`` (slots holding one of the first n_sink positions stay visible).
     q: [B, L, H_q, d_h]; k_cache, v_cache: [B, H_kv, S, d_h]; slot_pos: [B, S]
     (< 0 = empty); q_pos: [B, L].  Returns o [B, L, H_q, d_h], lse [B, H_q, L].
     """
@@ -120,11 +136,12 @@ def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None):
     lse = np.zeros((B, Hq, L), dtype=np.float64)
     for b in range(B):
         for t in range(L):
-            S_t = decode_index_set(slot_pos[b], int(q_pos[b, t]), W)
+            S_t = decode_index_set(slot_pos[b], int(q_pos[b, t]), W, n_sink)
             for h in range(Hq):
                 kvh = h // group
+                z = None if sink_logit is None else sink_logit[h]
                 o[b, t, h], lse[b, h, t] = attend(q[b, t, h], k_cache[b, kvh, S_t],
-                                                  v_cache[b, kvh, S_t], sc)
+                                                  v_cache[b, kvh, S_t], sc, z)
     return o, lse
 
 

@@ -53,7 +53,20 @@ def longformer_index_set(i: int, n: int, r: int, dilation: int = 1, globals_=())
     return np.asarray(sorted(window | set(G)), dtype=np.int64)
 
 
-def decode_index_set(slot_pos_row, cur: int, W: int) -> np.ndarray:
+def causal_sink_index_set(t: int, W: int, n_sink: int) -> np.ndarray:
+    """Causal window plus attention-sink tokens: the first n_sink positions stay
+    visible to every later query alongside its rolling window ([KB] §4,
+    "Failure mode 1": StreamingLLM keeps the first few KV slots pinned next to
+    the rolling window; [ST] "What's New": always-visible sink positions).
+    Union, each key once:
+    (t-W, t] together with {s : s < n_sink, s <= t}.
+    """
+    win = causal_index_set(t, W)
+    sinks = np.arange(min(n_sink, t + 1), dtype=np.int64)
+    return np.union1d(sinks, win).astype(np.int64)
+
+
+def decode_index_set(slot_pos_row, cur: int, W: int, n_sink: int = 0) -> np.ndarray:
     """Ring-cache slots attended by the query at absolute position ``cur``.
 
     The window is computed from the absolute token position stored in each slot,
@@ -62,9 +75,11 @@ def decode_index_set(slot_pos_row, cur: int, W: int) -> np.ndarray:
     it holds a position p with cur-W < p <= cur (the causal window of [KB] §2).
     Negative positions mark empty slots (a reading: the pages fix no sentinel).
     Returns slot indices.
+    With n_sink > 0, slots holding one of the first n_sink positions (p <= cur)
+    are attended too (pinned sink tokens, see ``causal_sink_index_set``).
     """
     sp = np.asarray(slot_pos_row, dtype=np.int64)
-    ok = (sp >= 0) & (sp > cur - W) & (sp <= cur)
+    ok = (sp >= 0) & (sp <= cur) & ((sp > cur - W) | (sp < n_sink))
     return np.nonzero(ok)[0].astype(np.int64)
 
 

@@ -44,16 +44,34 @@ def ring_from_sequence(k_seq, v_seq, upto, W):
     return k_cache, v_cache, slot_pos
 
 
-def ring_append(k_cache, v_cache, slot_pos, k_new, v_new, pos):
-    """Write a chunk of tokens per request into a ring of S slots, in place.
+def ring_slot(p: int, S: int, n_sink: int = 0) -> int:
+    """Slot of absolute position p in a cache of S slots.  Without sinks this is
+    the rolling buffer's p mod S ([KB] §2 "KV cache").  With n_sink pinned sink
+    tokens ([KB] §4 "Failure mode 1": the first few KV slots stay pinned next to a
+    rolling window) positions p < n_sink keep slot p and the rest roll over the
+    other S - n_sink slots (a reading: the pages fix no layout)."""
+    if p < n_sink:
+        return p
+    return n_sink + (p - n_sink) % (S - n_sink)
+
+
+def ring_append(k_cache, v_cache, slot_pos, k_new, v_new, pos, n_sink=0):
+    """Write a chunk of tokens per request into a cache of S slots, in place.
 
     The same rule as ``ring_write`` applied to each token in order: token t of
-    request b lands in slot pos[b, t] mod S ([KB] §2 "KV cache") and the slot
-    records pos[b, t] ([G3] "How it works").
+    request b lands in slot ``ring_slot(pos[b, t], S, n_sink)`` ([KB] §2 "KV
+    cache"; pos mod S without sinks) and the slot records pos[b, t] ([G3] "How
+    it works").
     k_cache, v_cache: [B, H_kv, S, d]; slot_pos: [B, S];
     k_new, v_new: [B, L, H_kv, d]; pos: [B, L] absolute positions.
     """
-    B, L = np.asarray(pos).shape
+    pos = np.asarray(pos)
+    B, L = pos.shape
+    S = slot_pos.shape[1]
     for t in range(L):
-        ring_write(k_cache, v_cache, slot_pos, k_new[:, t], v_new[:, t], np.asarray(pos)[:, t])
+        for b in range(B):
+            j = ring_slot(int(pos[b, t]), S, n_sink)
+            k_cache[b, :, j] = k_new[b, t]
+            v_cache[b, :, j] = v_new[b, t]
+            slot_pos[b, j] = int(pos[b, t])
 

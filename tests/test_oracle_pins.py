@@ -388,6 +388,82 @@ def test_prefill_cached_ignores_slot_order():
     np.testing.assert_allclose(o, o2, atol=1e-14)
 
 
+# ---------------------------------------------------------------- attention sinks
+
+@pytest.mark.parametrize("T,W,n_sink", [(40, 6, 4), (40, 1, 3), (33, 10, 1), (20, 30, 4)])
+def test_sink_window_against_sdpa_mask(T, W, n_sink):
+    # union of the causal window and the first n_sink tokens, through torch SDPA
+    # with the boolean mask written from the two definitions
+    B, Hq, Hkv, D = 2, 4, 2, 8
+    q, k, v = _rand((B, T, Hq, D), 80), _rand((B, T, Hkv, D), 81), _rand((B, T, Hkv, D), 82)
+    t = np.arange(T)[:, None]
+    s_ = np.arange(T)[None, :]
+    mask = ((s_ <= t) & (s_ > t - W)) | ((s_ < n_sink) & (s_ <= t))
+    o, _ = oracle.swa_prefill(q, k, v, W, n_sink=n_sink)
+    ref = _sdpa(q, k, v, False, mask=torch.from_numpy(mask))
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+    # each key once: the set sizes
+    for tt in range(T):
+        n = len(oracle.causal_sink_index_set(tt, W, n_sink))
+        assert n == min(tt + 1, W) + max(0, min(n_sink, tt + 1 - W))
+
+
+def test_sink_logit_closed_forms():
+    B, T, Hq, Hkv, D, W = 1, 12, 3, 1, 4, 5
+    rng = np.random.default_rng(83)
+    z = np.array([0.7, -2.0, 3.5])
+    v = np.full((B, T, Hkv, D), 1.5)
+    q = np.zeros((B, T, Hq, D))
+    k = rng.standard_normal((B, T, Hkv, D))
+    o, lse = oracle.swa_prefill(q, k, v, W, sink_logit=z)
+    for t in range(T):
+        n = min(t + 1, W)                       # q = 0: every score is 0
+        for h in range(Hq):
+            np.testing.assert_allclose(o[0, t, h], 1.5 * n / (n + math.exp(z[h])), rtol=1e-13)
+            np.testing.assert_allclose(lse[0, h, t], math.log(n + math.exp(z[h])), rtol=1e-13)
+    # lse with a sink = logaddexp(lse without, z); a very negative sink is no sink
+    q = rng.standard_normal((B, T, Hq, D))
+    o0, l0 = oracle.swa_prefill(q, k, v, W)
+    o1, l1 = oracle.swa_prefill(q, k, v, W, sink_logit=z)
+    np.testing.assert_allclose(l1, np.logaddexp(l0, z[None, :, None]), atol=1e-12)
+    np.testing.assert_allclose(o1, o0 * np.exp(l0 - l1).transpose(0, 2, 1)[..., None], atol=1e-12)
+    o2, _ = oracle.swa_prefill(q, k, v, W, sink_logit=np.full(Hq, -800.0))
+    np.testing.assert_allclose(o2, o0, atol=1e-15)
+
+
+def test_ring_slot_rule_with_sinks():
+    S, n_sink = 9, 3
+    kc = np.zeros((1, 1, S, 1)); vc = np.zeros_like(kc); sp = np.full((1, S), -1)
+    P = 40
+    pos = np.arange(P)[None]
+    oracle.ring_append(kc, vc, sp, pos[:, :, None, None].astype(float),
+                       -pos[:, :, None, None].astype(float), pos, n_sink=n_sink)
+    assert sp[0, :n_sink].tolist() == [0, 1, 2]                  # pinned
+    assert sorted(sp[0, n_sink:].tolist()) == list(range(P - (S - n_sink), P))  # rolling
+    assert [oracle.ring_slot(p, S, 0) for p in (0, 8, 9, 20)] == [0, 8, 0, 2]
+
+
+@pytest.mark.parametrize("W,L,p0,n_sink", [(8, 5, 30, 4), (16, 8, 40, 1), (6, 12, 9, 4)])
+def test_sink_ring_chunks_equal_prefill_rows(W, L, p0, n_sink):
+    # pinned sink slots + a rolling region of W + L - 1 slots, filled chunk by
+    # chunk, give the prefill rows with the same sinks and sink logits
+    B, T, Hq, Hkv, D = 2, p0 + L, 4, 2, 8
+    q, k, v = _rand((B, T, Hq, D), 84), _rand((B, T, Hkv, D), 85), _rand((B, T, Hkv, D), 86)
+    z = np.array([0.3, -1.0, 2.0, 0.0])
+    S = n_sink + W + L - 1
+    kc = np.zeros((B, Hkv, S, D)); vc = np.zeros_like(kc); sp = np.full((B, S), -1)
+    cuts = list(range(0, p0, 5)) + [p0, T]
+    for a, b_ in zip(cuts[:-1], cuts[1:]):
+        pos = np.tile(np.arange(a, b_), (B, 1))
+        oracle.ring_append(kc, vc, sp, k[:, a:b_], v[:, a:b_], pos, n_sink=n_sink)
+    qpos = np.tile(np.arange(p0, T), (B, 1))
+    o, lse = oracle.swa_prefill_cached(q[:, p0:T], kc, vc, sp, qpos, W, n_sink=n_sink,
+                                       sink_logit=z)
+    op, lp = oracle.swa_prefill(q, k, v, W, rows=list(range(p0, T)), n_sink=n_sink, sink_logit=z)
+    np.testing.assert_allclose(o, op, atol=1e-12)
+    np.testing.assert_allclose(lse, lp, atol=1e-12)
+
+
 # ---------------------------------------------------------------- tiles
 
 def test_tiles_hand_example():
