@@ -5,7 +5,7 @@ W=4096, H_q=32, H_kv=8, d_h=128, bf16 (band-TFLOP/s: 4*d_h FLOP per attended
 (query head, key) pair, masked tile work excluded).  The other workloads
 (causal prefill B=2 T=32768 W=1024 local-layer shape, ring decode B=64 W=4096,
 Longformer B=8 T=4096 r=256, chunked prefill of 512-token chunks over a ring
-cache) are reported in "extra".
+cache, prefill with attention sinks) are reported in "extra".
 
 Timing: inputs resident in HBM, W untimed warm-up launches, then K launches
 bracketed by torch.cuda.synchronize() and HIP events recorded on the stream the
@@ -13,7 +13,7 @@ kernels are launched on (torch's current stream, which the binding passes to
 the library).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only prefill|local|decode|longformer|chunk] [--profile-copy]
+                       [--only prefill|local|decode|longformer|chunk|sinks] [--profile-copy]
 """
 
 import argparse
@@ -114,6 +114,24 @@ def bench_prefill(c, steps, warmup):
     return dict(ms=ms, tflops=tflops, flops=flops, bytes=nbytes)
 
 
+def causal_sink_pairs(T, W, n_sink):
+    """Attended pairs per head with n_sink sink tokens: the window pairs plus, for
+    every row t >= W, the sinks s < n_sink that lie before its window."""
+    extra = sum(min(n_sink, t - W + 1) for t in range(W, T)) if n_sink else 0
+    return causal_pairs(T, W) + extra
+
+
+def bench_prefill_sinks(c, n_sink, steps, warmup):
+    q, k, v = (x.cuda() for x in inp.prefill_inputs(c))
+    z = torch.from_numpy(np.random.default_rng(c.seed + 7).standard_normal(c.Hq).astype(np.float32))
+    z = z.cuda()
+    o = torch.empty_like(q)
+    ms, _ = time_launches(lambda: bd.prefill_sinks(q, k, v, c.W, n_sink=n_sink, sink_logit=z, out=o),
+                          steps, warmup)
+    flops = 4.0 * c.D * c.Hq * c.B * causal_sink_pairs(c.T, c.W, n_sink)
+    return dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
+
+
 def bench_decode(c, steps, warmup):
     q, kc, vc, sp, cur = (x.cuda() for x in inp.decode_inputs(c))
     o = torch.empty_like(q)
@@ -187,7 +205,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "longformer", "local", "chunk"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "longformer", "local", "chunk",
+                                       "sinks"],
                     default="all", help="restrict to one workload (the headline always runs "
                     "unless decode/longformer/local is chosen)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -241,6 +260,14 @@ def main():
                      f"Hq={c6.Hq} Hkv={c6.Hkv} d_h={c6.D} bf16, chunk start in [{c6.p_lo}, {c6.p_hi})",
             value=round(r6["tflops"], 2), unit="TFLOP/s", ms=round(r6["ms"], 4),
             frac_mfma_peak=round(r6["tflops"] / PEAK_BF16_TFLOPS, 4), pairs=r6["pairs"])
+
+    if args.only in ("all", "sinks"):
+        r7 = bench_prefill_sinks(c2, 4, max(5, args.steps // 2), args.warmup)
+        extra["prefill_sinks"] = dict(
+            workload=f"causal SWA prefill with 4 sink tokens and per-head sink scores, "
+                     f"B={c2.B} T={c2.T} W={c2.W} Hq={c2.Hq} Hkv={c2.Hkv} d_h={c2.D} bf16",
+            value=round(r7["tflops"], 2), unit="TFLOP/s", ms=round(r7["ms"], 4),
+            frac_mfma_peak=round(r7["tflops"] / PEAK_BF16_TFLOPS, 4))
 
     if main_r is None:
         print(json.dumps({"partial": args.only, "extra": extra}), flush=True)

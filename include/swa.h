@@ -9,6 +9,8 @@
  * of "Sliding Window Attention: From Local Windows to Global Context"
  * (prathamp.com)).  The entry points differ only in S_t:
  *   swa_prefill     causal window  t-W < s <= t                (knowledge base §2, §3)
+ *   swa_prefill_sinks  the causal window plus pinned sink tokens and an optional
+ *                   per-head sink score (knowledge base §4; superteams.ai "What's New")
  *   swa_decode      ring cache of W slots, window from stored absolute positions
  *                   (knowledge base §2 "KV cache"; "Sliding Window Attention —
  *                   Gemma 3" study note, "How it works")
@@ -74,6 +76,21 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
                        float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
                        float scale, void *stream);
 
+/* Causal prefill with attention sinks.  Query t attends its window t-W < s <= t
+ * united with the first n_sink positions s < n_sink, s <= t, each key once
+ * (knowledge base §4 "Failure mode 1": StreamingLLM keeps the first few KV slots
+ * pinned next to the rolling window; superteams.ai "What's New": always-visible
+ * sink positions).  sink_logit (device float32 [H_q], or NULL) gives each query
+ * head a sink score z that joins the softmax denominator with no value:
+ *   o = sum_s exp(e_s) v_s / (exp(z) + sum_s exp(e_s)),  lse = log(exp(z) + sum_s exp(e_s))
+ * (a reading of the "learned per-head attention sink").  n_sink = 0 and a NULL
+ * sink_logit is swa_prefill.  Arguments otherwise as swa_prefill.
+ * Errors: as swa_prefill, plus INVALID for n_sink < 0, n_sink > 32 or a
+ * misaligned sink_logit. */
+swa_status swa_prefill_sinks(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                             float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                             int n_sink, const float *sink_logit, float scale, void *stream);
+
 /* Decode over a rolling-buffer KV cache: one new query token per request.
  * Token p is stored in slot p mod W (knowledge base §2 "KV cache"); every slot
  * records the absolute position it holds, and the window is computed from those
@@ -109,7 +126,10 @@ swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new,
  * goes to slot pos[b][t] mod S, which records slot_pos[b][slot] = pos[b][t]
  * (knowledge base §2 "KV cache"; Gemma 3 note, "How it works").  The same rule
  * as swa_cache_write applied to each token; a ring of S >= W + L - 1 slots
- * keeps every key the chunk's own queries need after the append.
+ * keeps every key the chunk's own queries need after the append.  With n_sink
+ * > 0 the first n_sink positions keep slots 0..n_sink-1 for good (pinned sink
+ * tokens, knowledge base §4 "Failure mode 1") and later positions p roll over
+ * the other slots: slot n_sink + (p - n_sink) mod (S - n_sink).
  *   k_new, v_new     : [B, L, H_kv, d_h]      pos : [B, L] int32 (device)
  *   k_cache, v_cache : [B, H_kv, S, d_h]      slot_pos : [B, S] int32
  * Preconditions (device data, not checked): pos >= 0 (negative tokens are
@@ -117,10 +137,10 @@ swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new,
  * request (true for consecutive positions with L <= S); otherwise which token
  * a shared slot keeps is unspecified.
  * Errors: INVALID for null pointers, B, L, S, H_kv < 1, L > S, B, L or H_kv >
- * 65535; UNSUPPORTED for other d_h. */
+ * 65535, n_sink < 0 or n_sink >= S; UNSUPPORTED for other d_h. */
 swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
                             const int32_t *pos, void *k_cache, void *v_cache, int32_t *slot_pos,
-                            int B, int L, int S, int H_kv, int d_h, void *stream);
+                            int B, int L, int S, int H_kv, int d_h, int n_sink, void *stream);
 
 /* Chunked prefill over a ring cache (multi-token decode).  Query token t of
  * request b has absolute position q_pos[b][t] and attends the slots j with
@@ -129,18 +149,21 @@ swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
  * "How it works": M = 1[s > t-W] 1[s < t+W] with the causal s <= t), so slot
  * order, stale, future and empty slots do not matter.  Write the chunk's own
  * keys first (swa_cache_append) to let its queries see each other causally.
- * A query with no valid slot gets o = 0 and lse = -inf.
+ * With n_sink > 0, slots holding one of the first n_sink positions (p <= q_pos)
+ * are attended too; sink_logit as in swa_prefill_sinks (NULL = none).
+ * A query with no valid slot gets o = 0 and lse = -inf (lse = z with a sink score).
  *   q, o             : [B, L, H_q, d_h]
  *   k_cache, v_cache : [B, H_kv, S, d_h]
  *   slot_pos         : [B, S] int32     q_pos : [B, L] int32, >= 0  (device)
  *   lse              : [B, H_q, L] float32 or NULL
  * No workspace.  Errors: INVALID for null pointers, B, L, S, H_q, H_kv < 1,
- * W < 1, H_q % H_kv != 0, bad scale; UNSUPPORTED for other d_h or (bf16) a
- * per-head cache slice of 2 GiB or more. */
+ * W < 1, H_q % H_kv != 0, bad scale, n_sink < 0, misaligned sink_logit;
+ * UNSUPPORTED for other d_h or (bf16) a per-head cache slice of 2 GiB or more. */
 swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *slot_pos, const int32_t *q_pos,
                               void *o, float *lse, int B, int L, int S, int H_q, int H_kv,
-                              int d_h, int W, float scale, void *stream);
+                              int d_h, int W, int n_sink, const float *sink_logit, float scale,
+                              void *stream);
 
 /* Longformer-style bidirectional attention.
  * A non-global row i of head h attends {i + k*dil[h] : -r <= k <= r} inside

@@ -41,9 +41,10 @@ def lib():
         L.swa_decode_workspace_size.restype = sz
         L.swa_decode.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
         L.swa_cache_write.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
-        L.swa_cache_append.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
-        L.swa_prefill_cached.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
-                                         vp]
+        L.swa_cache_append.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.swa_prefill_cached.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                         vp, f, vp]
+        L.swa_prefill_sinks.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, f, vp]
         L.swa_longformer_workspace_size.argtypes = [i, i, i, i, i]
         L.swa_longformer_workspace_size.restype = sz
         L.swa_longformer.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, f, vp, sz, vp]
@@ -105,6 +106,25 @@ def prefill(q, k, v, W, scale=None, out=None, return_lse=False):
     return (o, lse) if return_lse else o
 
 
+def prefill_sinks(q, k, v, W, n_sink=0, sink_logit=None, scale=None, out=None,
+                  return_lse=False):
+    """Causal window plus the first n_sink tokens and an optional per-head sink
+    score (sink_logit: float32 device tensor [Hq] or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    if sink_logit is not None:
+        _need(sink_logit, "sink_logit", 1)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(B, Hq, T, device=q.device, dtype=torch.float32) if return_lse else None
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().swa_prefill_sinks(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq,
+                                   Hkv, D, int(W), int(n_sink), _ptr(sink_logit), sc, _stream(q)),
+           "swa_prefill_sinks")
+    return (o, lse) if return_lse else o
+
+
 def decode_workspace_size(B, Hq, Hkv, W, D):
     return int(lib().swa_decode_workspace_size(B, Hq, Hkv, W, D))
 
@@ -139,20 +159,21 @@ def cache_write(k_new, v_new, pos, k_cache, v_cache, slot_pos):
            "swa_cache_write")
 
 
-def cache_append(k_new, v_new, pos, k_cache, v_cache, slot_pos):
-    """Append a chunk per request: k_new/v_new [B,L,Hkv,D], pos [B,L] -> slots pos mod S."""
+def cache_append(k_new, v_new, pos, k_cache, v_cache, slot_pos, n_sink=0):
+    """Append a chunk per request: k_new/v_new [B,L,Hkv,D], pos [B,L] -> slots pos mod S
+    (positions below n_sink keep their own slots; the rest roll over the others)."""
     _need(k_new, "k_new", 4)
     _need(v_new, "v_new", 4)
     _need(pos, "pos", 2)
     B, L, Hkv, D = k_new.shape
     S = k_cache.shape[2]
     _check(lib().swa_cache_append(_dt(k_new), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(k_cache),
-                                  _ptr(v_cache), _ptr(slot_pos), B, L, S, Hkv, D, _stream(k_new)),
-           "swa_cache_append")
+                                  _ptr(v_cache), _ptr(slot_pos), B, L, S, Hkv, D, int(n_sink),
+                                  _stream(k_new)), "swa_cache_append")
 
 
 def prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None, out=None,
-                   return_lse=False):
+                   return_lse=False, n_sink=0, sink_logit=None):
     """Chunked prefill over a ring cache: q [B,L,Hq,D], caches [B,Hkv,S,D],
     slot_pos [B,S], q_pos [B,L] -> o [B,L,Hq,D] (lse [B,Hq,L])."""
     _need(q, "q", 4)
@@ -167,7 +188,8 @@ def prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None, out=None
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib().swa_prefill_cached(_dt(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(slot_pos),
                                     _ptr(q_pos), _ptr(o), _ptr(lse), B, L, S, Hq, Hkv, D, int(W),
-                                    sc, _stream(q)), "swa_prefill_cached")
+                                    int(n_sink), _ptr(sink_logit), sc, _stream(q)),
+           "swa_prefill_cached")
     return (o, lse) if return_lse else o
 
 

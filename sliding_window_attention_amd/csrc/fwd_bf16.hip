@@ -28,6 +28,9 @@
 // mode, a chunk of queries with absolute positions against the slots of a ring
 // cache, slot attended iff its stored position p has q_pos-W < p <= q_pos
 // ([G3] "How it works": the window comes from positions, not buffer offsets).
+// Causal and ring modes take attention sinks: the first n_sink positions stay
+// visible next to the window ([KB] §4 "Failure mode 1"; [ST] "What's New"), and
+// an optional per-head sink score joins the softmax denominator.
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [PP] "Sliding Window Attention: From Local Windows to Global Context"
@@ -207,12 +210,14 @@ struct IntC {
 constexpr float kLazy = 8.f;
 
 // NW waves per workgroup; three waves per SIMD (12 per CU) bound the registers.
-// MODE: kCausal, kSymmetric or kRing (FwdMode).
+// MODE: kCausal, kSymmetric, kRing or kCausalSink (FwdMode).
 template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
     const FwdArgs a, const GlobalList gl) {
   constexpr bool SYM = MODE == kSymmetric;
   constexpr bool RING = MODE == kRing;
+  constexpr bool CSINK = MODE == kCausalSink;  // causal with sink tokens / scores
+  constexpr bool SCORE = CSINK || RING;        // may carry per-head sink scores
   using Gm = Geo<D>;
   // NST stages, each a row-major K tile followed by a V tile (swizzled
   // chunks); copies run NST-1 tiles ahead of the compute.  After the loop the
@@ -319,7 +324,9 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   tr.lo = uni(tr.lo);
   tr.hi = uni(tr.hi);
   const int n_win = tr.hi - tr.lo + 1;
-  const int n_glob = SYM ? ceil_div(a.G, BN) : 0;
+  // extra tiles after the window: global keys (symmetric), or key tile 0 for
+  // the sink tokens when the window tiles do not reach it (causal)
+  const int n_glob = SYM ? ceil_div(a.G, BN) : (CSINK && a.n_sink > 0 && tr.lo > 0) ? 1 : 0;
   const int n_tiles = n_win + n_glob;
   // this wave's valid rows [row0, w_last] and the window tiles they need
   const int w_last = min(row0 + kRowsPerWave, n_cls) - 1;
@@ -355,8 +362,9 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   // DMA of the K and V rows of tile j (window tiles j < n_win, then tiles of
   // global keys) into the stage at LDS address `stage`.
   auto issue = [&](int j, uint32_t stage) {
-    const bool whole = j < n_win && (tr.lo + j) * BN + BN <= n_keyrows;
-    const long long base = (k_rho + (long long)(tr.lo + j) * BN * k_rowstride) * 2;
+    const int kt = (j < n_win) ? tr.lo + j : 0;  // key tile (sink tile: 0)
+    const bool whole = (j < n_win || !SYM) && kt * BN + BN <= n_keyrows;
+    const long long base = (k_rho + (long long)kt * BN * k_rowstride) * 2;
 #pragma unroll
     for (int t = 0; t < NSLOT; ++t) {
       const int i = wave + t * NW;
@@ -373,8 +381,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           const int r = (i % Gm::NI) * Gm::RPI + lane / Gm::CPR;
           const int p = lane % Gm::CPR;
           long long o;
-          if (j < n_win) {
-            const int sr = min((tr.lo + j) * BN + r, n_keyrows - 1);
+          if (j < n_win || !SYM) {
+            const int sr = min(kt * BN + r, n_keyrows - 1);
             o = (k_rho + (long long)sr * k_rowstride) * 2;
           } else {
             const int u = min((j - n_win) * BN + r, a.G - 1);
@@ -552,7 +560,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = pv[i];
-          const bool ok = k0 + i < n_in && p >= 0 && p > my_pos - a.W && p <= my_pos;
+          const bool ok = k0 + i < n_in && p >= 0 && p <= my_pos &&
+                          (p > my_pos - a.W || p < a.n_sink);
           if (!ok) sv[kb][4 * g4 + i] = -INFINITY;
         }
       }
@@ -570,12 +579,37 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       // this lane's bounds shifted to the same origin
       const int base = (tr.lo + j) * BN + 4 * lh;
       const int lo = lo_key - base, hi = hi_key - base;
+      if (CSINK && a.n_sink > 0 && tr.lo + j == 0) {
+        // key tile 0 inside the window range: sinks s < n_sink, s <= t join
+        const int hs = min(a.n_sink - 1, my_row) - base;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+            if ((c < lo || c > hi) && c > hs) sv[kb][e] = -INFINITY;
+          }
+        return;
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
           if (c < lo || c > hi) sv[kb][e] = -INFINITY;
+        }
+      return;
+    }
+    if constexpr (!SYM) {
+      if constexpr (!CSINK) return;
+      // the sink tile (key tile 0, outside every row's window): s < n_sink
+      const int hs = a.n_sink - 1 - 4 * lh;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+          if (c > hs) sv[kb][e] = -INFINITY;
         }
       return;
     }
@@ -615,7 +649,9 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     __syncthreads();
     if (j + NST - 1 < n_tiles) issue(j + NST - 1, a_s0 + (uint32_t)(((st + NST - 1) % NST) * STAGE_B));
     const int kj = tr.lo + j;
-    if (has_rows && (j >= n_win || (kj >= wr.lo && kj <= wr.hi))) {
+    // a wave computes the tiles of its rows' band, the extra tiles, and key
+    // tile 0 when sink tokens live there
+    if (has_rows && (j >= n_win || (kj >= wr.lo && kj <= wr.hi) || (CSINK && a.n_sink > 0 && kj == 0))) {
       const char *ks = smem + st * STAGE_B;
       f32x16 sv[KB];
       U4 pu[PK];
@@ -646,7 +682,19 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   __syncthreads();
 
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
-  const float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
+  // With a sink score z (natural-log units) the denominator gains exp(z): in
+  // the log2 domain of m, l that is 2^(z log2 e - m), taken against the larger
+  // of m and z log2 e so neither side overflows.
+  float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
+  float lse_l2 = (l_run > 0.f) ? m_run + __log2f(l_run) : -INFINITY;  // log2 units
+  if (SCORE && a.sink_logit) {
+    const float z2 = a.sink_logit[h] * 1.4426950408889634f;
+    const float mu = (m_run == -INFINITY) ? z2 : fmaxf(m_run, z2);
+    const float sc = (l_run > 0.f) ? __builtin_amdgcn_exp2f(m_run - mu) : 0.f;
+    const float lt = l_run * sc + __builtin_amdgcn_exp2f(z2 - mu);
+    inv_l = sc / lt;
+    lse_l2 = mu + __log2f(lt);
+  }
   // Each wave stages its 32 rows (row-major, 16-byte chunks XOR-swizzled by
   // row, no padding) in its own slice of the now idle stage memory.
   uint16_t *ost = reinterpret_cast<uint16_t *>(smem + wave * kRowsPerWave * D * 2);
@@ -666,7 +714,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     }
   if (a.lse && lh == 0 && my_row < n_cls) {
     const long long t_abs = rho + (long long)dil * my_row;
-    const float lse = (l_run > 0.f) ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    const float lse = lse_l2 * 0.69314718055994531f;
     a.lse[((long long)b * a.Hq + h) * a.T + t_abs] = lse;
   }
   __syncthreads();
@@ -698,6 +746,9 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *
   if (mode == kCausal) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausal, NWC>), grid, block, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_kernel<64, kCausal, NWC>), grid, block, 0, st, a, *gl);
+  } else if (mode == kCausalSink) {
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausalSink, NWC>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, kCausalSink, NWC>), grid, block, 0, st, a, *gl);
   } else if (mode == kRing) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kRing, NWC>), grid, block, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_kernel<64, kRing, NWC>), grid, block, 0, st, a, *gl);

@@ -10,8 +10,10 @@
 // row attends every position, any other row attends i + k*dil (|k| <= r) inside
 // [0, T) plus the global positions not already in that window ([PP] §1.1,
 // §3.1, §4.3); ring: a query at absolute position p attends the ring slots
-// holding a position in (p-W, p] ([G3] "How it works").  Scores use the
-// masked softmax of [KB] §2.
+// holding a position in (p-W, p] ([G3] "How it works").  Causal and ring
+// modes take attention sinks: the first n_sink positions stay visible ([KB] §4
+// "Failure mode 1"; [ST] "What's New") and a per-head sink score may join the
+// denominator.  Scores use the masked softmax of [KB] §2.
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com);
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   if (!live) return;
 
   // Enumerate the connectivity set as idx -> key position (or -1 = skip).
-  int n_keys, base = 0, kstep = 1, n_win = 0;
+  int n_keys, base = 0, kstep = 1, n_win = 0, n_sk = 0;
   bool is_glob = false;
   const int dil = SYM ? a.dil[h] : 1;
   int my_pos = 0;
@@ -54,7 +56,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
     my_pos = a.q_pos[(long long)b * a.T + t];
   } else if constexpr (!SYM) {
     base = max(0, t - a.W + 1);
-    n_keys = t - base + 1;
+    n_sk = min(a.n_sink, base);  // sink tokens before the window
+    n_keys = n_sk + t - base + 1;
   } else {
     for (int g = 0; g < a.G; ++g) is_glob |= gl.idx[b * a.G + g] == t;
     if (is_glob) {
@@ -79,8 +82,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
     if (idx < n_keys) {
       if constexpr (RING) {
         const int p = a.slot_pos[(long long)b * a.S + idx];
-        key = (p >= 0 && p > my_pos - a.W && p <= my_pos) ? idx : -1;
-      } else if (!SYM || is_glob) key = base + idx * kstep;
+        key = (p >= 0 && p <= my_pos && (p > my_pos - a.W || p < a.n_sink)) ? idx : -1;
+      } else if constexpr (!SYM) {
+        key = (idx < n_sk) ? idx : base + (idx - n_sk);
+      } else if (is_glob) key = base + idx * kstep;
       else if (idx < n_win) key = base + idx * kstep;
       else {
         const int g = gl.idx[b * a.G + idx - n_win];
@@ -120,12 +125,22 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
       }
     }
   }
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  float inv = (l > 0.f) ? 1.f / l : 0.f;
+  float lse2 = (l > 0.f) ? m + log2f(l) : -INFINITY;  // log2 units
+  if (!SYM && a.sink_logit) {
+    // the sink score z joins the denominator: 2^(z log2 e - m) against max(m, z)
+    const float z2 = a.sink_logit[h] * 1.4426950408889634f;
+    const float mu = (m == -INFINITY) ? z2 : fmaxf(m, z2);
+    const float sc = (l > 0.f) ? exp2f(m - mu) : 0.f;
+    const float lt = l * sc + exp2f(z2 - mu);
+    inv = sc / lt;
+    lse2 = mu + log2f(lt);
+  }
   float *o = static_cast<float *>(a.o) + (long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[lane + 64 * i] = acc[i] * inv;
   if (a.lse && lane == 0)
-    a.lse[((long long)b * a.Hq + h) * a.T + t] = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    a.lse[((long long)b * a.Hq + h) * a.T + t] = lse2 * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -136,7 +151,7 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *g
   const int blocks = (int)((rows + 3) / 4);
   if (blocks <= 0) return hipSuccess;
   const dim3 g(blocks), blk(256);
-  if (mode == kCausal) {
+  if (mode == kCausal || mode == kCausalSink) {  // one kernel; sinks are runtime here
     if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kCausal>), g, blk, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_f32_kernel<64, kCausal>), g, blk, 0, st, a, *gl);
   } else if (mode == kRing) {

@@ -535,15 +535,19 @@ hipError_t run(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) 
 }
 
 // Ring append ([KB] §2 "KV cache": token i lives in slot i mod S; the slot
-// records its absolute position, [G3] "How it works").  Block (hk, t, b) copies
+// records its absolute position, [G3] "How it works").  With n_sink pinned sink
+// tokens ([KB] §4 "Failure mode 1") positions below n_sink keep their own slots
+// and the rest roll over the remaining S - n_sink.  Block (hk, t, b) copies
 // token t's key and value rows of head hk; the chunk's slots are distinct (a
 // documented precondition), so blocks never write the same slot.
 __global__ void cache_write_kernel(const char *kn, const char *vn, const int *pos, char *kc,
-                                   char *vc, int *slot_pos, int L, int S, int Hkv, int row_bytes) {
+                                   char *vc, int *slot_pos, int L, int S, int Hkv, int row_bytes,
+                                   int n_sink) {
   const int hk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int p = pos[(long long)b * L + t];
   if (p < 0) return;  // documented precondition; never index with a negative slot
-  const int slot = p % S;
+  // sink tokens (p < n_sink) keep slot p; the rest roll over the other slots
+  const int slot = (p < n_sink) ? p : n_sink + (p - n_sink) % (S - n_sink);
   const long long src = (((long long)b * L + t) * Hkv + hk) * row_bytes;
   const long long dst = (((long long)b * Hkv + hk) * S + slot) * row_bytes;
   for (int i = threadIdx.x * 4; i < row_bytes; i += blockDim.x * 4) {
@@ -589,12 +593,12 @@ int split_max_chunk() { return kMaxChunk; }
 
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
                               void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,
-                              hipStream_t st) {
+                              int n_sink, hipStream_t st) {
   const int row_bytes = D * (f32 ? 4 : 2);
   hipLaunchKernelGGL(cache_write_kernel, dim3(Hkv, L, B), dim3(64), 0, st,
                      static_cast<const char *>(kn), static_cast<const char *>(vn), pos,
                      static_cast<char *>(kc), static_cast<char *>(vc), slot_pos, L, S, Hkv,
-                     row_bytes);
+                     row_bytes, n_sink);
   return hipGetLastError();
 }
 

@@ -125,7 +125,16 @@ int swa_band_tiles(int mode, int T, int w_or_r, int BM, int BN, int32_t *out, in
 swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
                        float *lse, int B, int T, int H_q, int H_kv, int d_h, int W, float scale,
                        void *stream) {
+  return swa_prefill_sinks(dt, q, k, v, o, lse, B, T, H_q, H_kv, d_h, W, 0, nullptr, scale,
+                           stream);
+}
+
+swa_status swa_prefill_sinks(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                             float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                             int n_sink, const float *sink_logit, float scale, void *stream) {
   if (!dt_ok(dt) || !q || !k || !v || !o) return SWA_ERR_INVALID;
+  if (n_sink < 0 || n_sink > kMaxSinks || (sink_logit && !aligned(sink_logit, 4)))
+    return SWA_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
     return SWA_ERR_INVALID;
@@ -142,6 +151,8 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
   a.k_st = (long long)H_kv * d_h;
   a.k_sb = a.k_st * T;
   a.k_sh = d_h;
+  a.n_sink = n_sink;
+  a.sink_logit = sink_logit;
   a.W = W;
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
@@ -153,19 +164,22 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, kCausal, d_h, &gl, st));
+  const int mode = (n_sink > 0 || sink_logit) ? kCausalSink : kCausal;
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, mode, d_h, &gl, st));
   // bf16 kernels address one batch slice of K/V with 32-bit byte offsets
   if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31))
     return SWA_ERR_UNSUPPORTED;
-  return hip_status(launch_fwd_bf16(a, kCausal, d_h, &gl, st));
+  return hip_status(launch_fwd_bf16(a, mode, d_h, &gl, st));
 }
 
 swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *slot_pos, const int32_t *q_pos,
                               void *o, float *lse, int B, int L, int S, int H_q, int H_kv,
-                              int d_h, int W, float scale, void *stream) {
+                              int d_h, int W, int n_sink, const float *sink_logit, float scale,
+                              void *stream) {
   if (!dt_ok(dt) || !q || !k_cache || !v_cache || !slot_pos || !q_pos || !o)
     return SWA_ERR_INVALID;
+  if (n_sink < 0 || (sink_logit && !aligned(sink_logit, 4))) return SWA_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
       !aligned(slot_pos, 4) || !aligned(q_pos, 4) || (lse && !aligned(lse, 4)))
     return SWA_ERR_INVALID;
@@ -193,6 +207,8 @@ swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
   a.slot_pos = slot_pos;
   a.q_pos = q_pos;
   a.S = S;
+  a.n_sink = n_sink;
+  a.sink_logit = sink_logit;
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -256,23 +272,24 @@ swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new, c
   if (B < 1 || W < 1 || H_kv < 1 || B > 65535) return SWA_ERR_INVALID;
   if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
   return hip_status(launch_cache_write(dt == SWA_F32, k_new, v_new, pos, k_cache, v_cache,
-                                       slot_pos, B, 1, W, H_kv, d_h,
+                                       slot_pos, B, 1, W, H_kv, d_h, 0,
                                        static_cast<hipStream_t>(stream)));
 }
 
 swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
                             const int32_t *pos, void *k_cache, void *v_cache, int32_t *slot_pos,
-                            int B, int L, int S, int H_kv, int d_h, void *stream) {
+                            int B, int L, int S, int H_kv, int d_h, int n_sink, void *stream) {
   if (!dt_ok(dt) || !k_new || !v_new || !pos || !k_cache || !v_cache || !slot_pos)
     return SWA_ERR_INVALID;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
       !aligned(v_cache, 16) || !aligned(pos, 4) || !aligned(slot_pos, 4))
     return SWA_ERR_INVALID;
-  if (B < 1 || L < 1 || S < 1 || L > S || H_kv < 1 || L > 65535 || H_kv > 65535 || B > 65535)
+  if (B < 1 || L < 1 || S < 1 || L > S || H_kv < 1 || L > 65535 || H_kv > 65535 || B > 65535 ||
+      n_sink < 0 || n_sink >= S)
     return SWA_ERR_INVALID;
   if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
   return hip_status(launch_cache_write(dt == SWA_F32, k_new, v_new, pos, k_cache, v_cache,
-                                       slot_pos, B, L, S, H_kv, d_h,
+                                       slot_pos, B, L, S, H_kv, d_h, n_sink,
                                        static_cast<hipStream_t>(stream)));
 }
 

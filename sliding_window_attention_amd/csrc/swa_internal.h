@@ -165,10 +165,16 @@ struct FwdArgs {
   const int *slot_pos;   // [B, S] position held by each slot (< 0 = empty)
   const int *q_pos;      // [B, T] absolute position of each query row
   int S;                 // ring slots (key rows per batch and head)
+  // attention sinks (causal and ring modes)
+  int n_sink;                // the first n_sink positions stay visible (<= kMaxSinks)
+  const float *sink_logit;   // [H_q] per-head sink score in the denominator, or null
 };
 
-// Window families of the banded kernels.
-enum FwdMode { kCausal = 0, kSymmetric = 1, kRing = 2 };
+constexpr int kMaxSinks = 32;  // sink tokens fit the first key tile
+
+// Window families of the banded kernels (kCausalSink: causal plus attention
+// sinks, a separate instantiation so the plain causal kernel carries none of it).
+enum FwdMode { kCausal = 0, kSymmetric = 1, kRing = 2, kCausalSink = 3 };
 
 struct GlobalList {
   int idx[kMaxGlobalsLF];  // [B][G] positions
@@ -201,7 +207,7 @@ hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const 
                         int G, int H, hipStream_t st);
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
                               void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,
-                              hipStream_t st);
+                              int n_sink, hipStream_t st);
 hipError_t launch_debug_mask(int mode, int T, int w_or_r, int dil, const GlobalList *gl, int G,
                              uint8_t *mask, hipStream_t st);
 

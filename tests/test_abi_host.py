@@ -121,11 +121,11 @@ def test_cache_write_and_debug_validation():
 
 def _cached(**kw):
     a = dict(dt=0, q=P, kc=P, vc=P, sp=P, qp=P, o=P, lse=None, B=2, L=5, S=40, Hq=4, Hkv=2,
-             D=128, W=16, sc=0.1)
+             D=128, W=16, ns=0, z=None, sc=0.1)
     a.update(kw)
     return bd.lib().swa_prefill_cached(a["dt"], a["q"], a["kc"], a["vc"], a["sp"], a["qp"],
                                        a["o"], a["lse"], a["B"], a["L"], a["S"], a["Hq"],
-                                       a["Hkv"], a["D"], a["W"], a["sc"], S0)
+                                       a["Hkv"], a["D"], a["W"], a["ns"], a["z"], a["sc"], S0)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -133,7 +133,7 @@ def _cached(**kw):
     (dict(qp=ctypes.c_void_p(4098)), INVALID), (dict(kc=ctypes.c_void_p(4104)), INVALID),
     (dict(B=0), INVALID), (dict(L=0), INVALID), (dict(S=0), INVALID), (dict(W=0), INVALID),
     (dict(Hq=5), INVALID), (dict(sc=-1.0), INVALID), (dict(dt=3), INVALID),
-    (dict(D=32), UNSUPPORTED),
+    (dict(D=32), UNSUPPORTED), (dict(ns=-1), INVALID), (dict(z=ctypes.c_void_p(4098)), INVALID),
     (dict(dt=0, S=1 << 23, D=128), UNSUPPORTED),   # bf16 head slice of 2 GiB
 ])
 def test_prefill_cached_validation(kw, code):
@@ -142,13 +142,13 @@ def test_prefill_cached_validation(kw, code):
 
 def test_cache_append_validation():
     L = bd.lib()
-    ok = dict(dt=0, kn=P, vn=P, pos=P, kc=P, vc=P, sp=P, B=2, L=4, S=8, Hkv=2, D=64)
+    ok = dict(dt=0, kn=P, vn=P, pos=P, kc=P, vc=P, sp=P, B=2, L=4, S=8, Hkv=2, D=64, ns=0)
 
     def call(**kw):
         a = dict(ok)
         a.update(kw)
         return L.swa_cache_append(a["dt"], a["kn"], a["vn"], a["pos"], a["kc"], a["vc"], a["sp"],
-                                  a["B"], a["L"], a["S"], a["Hkv"], a["D"], S0)
+                                  a["B"], a["L"], a["S"], a["Hkv"], a["D"], a["ns"], S0)
 
     assert call(sp=None) == INVALID
     assert call(kn=ctypes.c_void_p(4100)) == INVALID
@@ -156,6 +156,21 @@ def test_cache_append_validation():
     assert call(L=9) == INVALID          # more tokens than slots
     assert call(B=70000) == INVALID
     assert call(D=100) == UNSUPPORTED
+    assert call(ns=-1) == INVALID
+    assert call(ns=8) == INVALID         # no rolling slot left
+
+
+def test_prefill_sinks_validation():
+    L = bd.lib()
+
+    def call(ns=4, z=None, D=128, W=8):
+        return L.swa_prefill_sinks(0, P, P, P, P, None, 1, 16, 4, 2, D, W, ns, z, 0.1, S0)
+
+    assert call(ns=-1) == INVALID
+    assert call(ns=33) == INVALID        # sinks must fit the first key tile
+    assert call(z=ctypes.c_void_p(4098)) == INVALID
+    assert call(W=0) == INVALID
+    assert call(D=96) == UNSUPPORTED
 
 
 def test_tile_config():
