@@ -79,8 +79,8 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
 /* Causal prefill with attention sinks.  Query t attends its window t-W < s <= t
  * united with the first n_sink positions s < n_sink, s <= t, each key once
  * (knowledge base §4 "Failure mode 1": StreamingLLM keeps the first few KV slots
- * pinned next to the rolling window; superteams.ai "What's New": always-visible
- * sink positions).  sink_logit (device float32 [H_q], or NULL) gives each query
+ * pinned next to the rolling window; superteams.ai "What's New": sink positions
+ * that every query sees).  sink_logit (device float32 [H_q], or NULL) gives each query
  * head a sink score z that joins the softmax denominator with no value:
  *   o = sum_s exp(e_s) v_s / (exp(z) + sum_s exp(e_s)),  lse = log(exp(z) + sum_s exp(e_s))
  * (a reading of the "learned per-head attention sink").  n_sink = 0 and a NULL

@@ -57,7 +57,7 @@ def causal_sink_index_set(t: int, W: int, n_sink: int) -> np.ndarray:
     """Causal window plus attention-sink tokens: the first n_sink positions stay
     visible to every later query alongside its rolling window ([KB] §4,
     "Failure mode 1": StreamingLLM keeps the first few KV slots pinned next to
-    the rolling window; [ST] "What's New": always-visible sink positions).
+    the rolling window; [ST] "What's New": sink positions every query sees).
     Union, each key once:
     (t-W, t] together with {s : s < n_sink, s <= t}.
     """
