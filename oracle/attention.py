@@ -145,15 +145,25 @@ def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None, n_si
     return o, lse
 
 
-def swa_longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, rows=None, heads=None):
+def swa_longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, rows=None, heads=None,
+                   qg=None, kg=None, vg=None):
     """Longformer-style bidirectional attention: per-head dilated window + globals.
 
     q, k, v: [B, T, H, d_h]; dilation: [H] ints >= 1 (None = all 1);
     global_idx: [B, G] positions (None or G = 0 = no globals).
     S_i follows ``longformer_index_set`` ([PP] §1.1, §3.1, §4.3).
     ``rows``/``heads`` optionally restrict the computation.
+
+    ``qg, kg, vg`` ([B, T, H, d_h], all three or none): the separate global
+    projections of [PP] §5.2.  A global row uses qg for its query and kg, vg for
+    every position; a local row keeps its sliding query q, reads its window
+    positions that are not global through k, v, and every global position
+    through kg, vg.  With qg, kg, vg equal to q, k, v this is the shared form
+    ([PP] §5.3: the global projections start as copies of the sliding ones).
     Returns o [B, R, H', d_h], lse [B, H', R].
     """
+    if qg is not None:
+        return _longformer_two_proj(q, k, v, qg, kg, vg, r, dilation, global_idx, scale, rows, heads)
     B, T, H, D = q.shape
     sc = _default_scale(D, scale)
     dil = [1] * H if dilation is None else [int(x) for x in dilation]
@@ -167,6 +177,30 @@ def swa_longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, rows=
             for ri, i in enumerate(rows):
                 S = longformer_index_set(int(i), T, r, dil[h], G)
                 o[b, ri, hi], lse[b, hi, ri] = attend(q[b, i, h], k[b, S, h], v[b, S, h], sc)
+    return o, lse
+
+
+def _longformer_two_proj(q, k, v, qg, kg, vg, r, dilation, global_idx, scale, rows, heads):
+    B, T, H, D = q.shape
+    sc = _default_scale(D, scale)
+    dil = [1] * H if dilation is None else [int(x) for x in dilation]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = list(range(H)) if heads is None else list(heads)
+    o = np.zeros((B, len(rows), len(heads), v.shape[-1]), dtype=np.float64)
+    lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
+    for b in range(B):
+        G = [] if global_idx is None else sorted(int(g) for g in np.asarray(global_idx)[b])
+        for hi, h in enumerate(heads):
+            for ri, i in enumerate(rows):
+                if i in G:                          # [PP] §5.2: Q_g against K_g, V_g of all
+                    o[b, ri, hi], lse[b, hi, ri] = attend(qg[b, i, h], kg[b, :, h], vg[b, :, h], sc)
+                    continue
+                S = longformer_index_set(int(i), T, r, dil[h], G)
+                local = np.array([j for j in S if j not in G], dtype=np.int64)
+                Kx = np.concatenate([_f64(k[b, local, h]).reshape(-1, D), _f64(kg[b, G, h]).reshape(-1, D)])
+                Vx = np.concatenate([_f64(v[b, local, h]).reshape(-1, v.shape[-1]),
+                                     _f64(vg[b, G, h]).reshape(-1, v.shape[-1])])
+                o[b, ri, hi], lse[b, hi, ri] = attend(q[b, i, h], Kx, Vx, sc)
     return o, lse
 
 

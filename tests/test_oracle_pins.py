@@ -464,6 +464,54 @@ def test_sink_ring_chunks_equal_prefill_rows(W, L, p0, n_sink):
     np.testing.assert_allclose(lse, lp, atol=1e-12)
 
 
+# ---------------------------------------------------------------- Longformer global projections
+
+def test_global_projections_equal_to_sliding_is_shared_form():
+    # [PP] §5.3: global projections initialised from the sliding ones behave
+    # exactly like the shared form
+    B, T, H, D, r = 2, 24, 3, 8, 2
+    q, k, v = _rand((B, T, H, D), 100), _rand((B, T, H, D), 101), _rand((B, T, H, D), 102)
+    g = np.array([[0, 8, 13], [5, 6, 20]])
+    dil = [1, 2, 3]
+    o1, l1 = oracle.swa_longformer(q, k, v, r, dil, g)
+    o2, l2 = oracle.swa_longformer(q, k, v, r, dil, g, qg=q.copy(), kg=k.copy(), vg=v.copy())
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, atol=1e-13)
+
+
+def test_global_projections_against_sdpa_on_stacked_keys():
+    # Independent route: stack the two projections into 2T key/value rows
+    # ([k; kg], [v; vg]) and give torch SDPA one boolean mask per row: a local
+    # row sees its window positions that are not global in the first half and
+    # every global position in the second half; a global row sees the whole
+    # second half with its qg query.
+    B, T, H, D, r = 1, 20, 2, 8, 2
+    q, k, v = _rand((B, T, H, D), 103), _rand((B, T, H, D), 104), _rand((B, T, H, D), 105)
+    qg, kg, vg = _rand((B, T, H, D), 106), _rand((B, T, H, D), 107), _rand((B, T, H, D), 108)
+    G = [0, 9]
+    dil = [1, 2]
+    o, _ = oracle.swa_longformer(q, k, v, r, dil, np.array([G]), qg=qg, kg=kg, vg=vg)
+    for h in range(H):
+        d = dil[h]
+        mask = np.zeros((T, 2 * T), dtype=bool)
+        qrows = np.zeros((T, D))
+        for i in range(T):
+            if i in G:
+                mask[i, T:] = True
+                qrows[i] = qg[0, i, h]
+            else:
+                for j in range(T):
+                    if (i - j) % d == 0 and abs(i - j) <= r * d and j not in G:
+                        mask[i, j] = True
+                for gpos in G:
+                    mask[i, T + gpos] = True
+                qrows[i] = q[0, i, h]
+        K2 = np.concatenate([k[0, :, h], kg[0, :, h]])[None, :, None]
+        V2 = np.concatenate([v[0, :, h], vg[0, :, h]])[None, :, None]
+        ref = _sdpa(qrows[None, :, None], K2, V2, False, mask=torch.from_numpy(mask))
+        np.testing.assert_allclose(o[0, :, h], ref[0, :, 0], atol=1e-12)
+
+
 # ---------------------------------------------------------------- tiles
 
 def test_tiles_hand_example():
