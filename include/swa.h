@@ -184,7 +184,28 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
                           const int32_t *dilation, const int32_t *global_idx, int G,
                           float scale, void *workspace, size_t workspace_bytes, void *stream);
 
-/* ---- introspection (tests) ------------------------------------------------ */
+/* Longformer-style attention with separate global projections (prathamp.com
+ * §5.2: the global attention has its own query, key and value projections;
+ * knowledge base §2 names Q_g, K_g, V_g).  The connectivity sets are those of
+ * swa_longformer; what changes is which projection each pair reads:
+ *   global row i (i in G_b): query qg_i against kg_s, vg_s for every s in [0, T);
+ *   any other row i: query q_i against k_j, v_j for the window positions j
+ *     that are not global, and against kg_g, vg_g for every global position g.
+ * With qg, kg, vg equal to q, k, v this is swa_longformer (prathamp.com §5.3:
+ * the global projections start as copies of the sliding ones).
+ *   qg, kg, vg : [B, T, H, d_h] device, same dtype and layout as q, k, v
+ *                (only the global rows of qg are read; kg, vg are read whole
+ *                when G > 0)
+ * Every other argument, the workspace size (swa_longformer_workspace_size)
+ * and the errors are those of swa_longformer; null qg, kg or vg is INVALID. */
+swa_status swa_longformer_proj(swa_dtype dt, const void *q, const void *k, const void *v,
+                               const void *qg, const void *kg, const void *vg, void *o,
+                               float *lse, int B, int T, int H, int d_h, int r,
+                               const int32_t *dilation, const int32_t *global_idx, int G,
+                               float scale, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* ---- introspection (tests)------------------------------------------------ */
 
 /* Query/key tile sizes (rows per workgroup, keys per tile) the bf16 kernels use
  * for this entry point ('p' prefill, 'l' longformer) and head shape. */

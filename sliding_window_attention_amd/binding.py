@@ -48,13 +48,16 @@ def lib():
         L.swa_longformer_workspace_size.argtypes = [i, i, i, i, i]
         L.swa_longformer_workspace_size.restype = sz
         L.swa_longformer.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, f, vp, sz, vp]
+        L.swa_longformer_proj.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp,
+                                          i, f, vp, sz, vp]
         L.swa_tile_config.argtypes = [i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         L.swa_band_tiles.argtypes = [i, i, i, i, i, vp, i]
         L.swa_debug_index_mask.argtypes = [i, i, i, i, vp, i, vp, vp]
         L.swa_status_str.argtypes = [i]
         L.swa_status_str.restype = ctypes.c_char_p
-        for name in ("swa_prefill", "swa_decode", "swa_cache_write", "swa_longformer",
-                     "swa_tile_config", "swa_debug_index_mask"):
+        for name in ("swa_prefill", "swa_prefill_sinks", "swa_prefill_cached", "swa_decode",
+                     "swa_cache_write", "swa_cache_append", "swa_longformer",
+                     "swa_longformer_proj", "swa_tile_config", "swa_debug_index_mask"):
             getattr(L, name).restype = i
         L.swa_band_tiles.restype = i
         L.swa_version.restype = i
@@ -198,13 +201,23 @@ def longformer_workspace_size(B, T, H, D, G):
 
 
 def longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, out=None, workspace=None,
-               return_lse=False):
+               return_lse=False, qg=None, kg=None, vg=None):
     """Bidirectional window |i-j| <= r (per-head dilation) plus global tokens.
 
     dilation: host int sequence [H] or None; global_idx: host int array [B, G] or None.
+    qg, kg, vg (all three or none, shaped like q): separate global projections
+    (swa_longformer_proj).
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, 4)
+    proj = (qg, kg, vg)
+    if any(x is not None for x in proj):
+        if any(x is None for x in proj):
+            raise ValueError("qg, kg and vg go together")
+        for t, n in zip(proj, ("qg", "kg", "vg")):
+            _need(t, n, 4)
+            if t.shape != q.shape or t.dtype != q.dtype:
+                raise ValueError(f"{n} must match q in shape and dtype")
     B, T, H, D = q.shape
     dil = None
     if dilation is not None:
@@ -225,9 +238,15 @@ def longformer(q, k, v, r, dilation=None, global_idx=None, scale=None, out=None,
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib().swa_longformer(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                B, T, H, D, int(r), dil, gl, G, sc, _ptr(ws), ws_bytes,
-                                _stream(q)), "swa_longformer")
+    if qg is None:
+        _check(lib().swa_longformer(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                    B, T, H, D, int(r), dil, gl, G, sc, _ptr(ws), ws_bytes,
+                                    _stream(q)), "swa_longformer")
+    else:
+        _check(lib().swa_longformer_proj(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(qg), _ptr(kg),
+                                         _ptr(vg), _ptr(o), _ptr(lse), B, T, H, D, int(r), dil,
+                                         gl, G, sc, _ptr(ws), ws_bytes, _stream(q)),
+               "swa_longformer_proj")
     return (o, lse) if return_lse else o
 
 

@@ -30,7 +30,9 @@
 // ([G3] "How it works": the window comes from positions, not buffer offsets).
 // Causal and ring modes take attention sinks: the first n_sink positions stay
 // visible next to the window ([KB] §4 "Failure mode 1"; [ST] "What's New"), and
-// an optional per-head sink score joins the softmax denominator.
+// an optional per-head sink score joins the softmax denominator.  Symmetric
+// mode may take separate global projections ([PP] §5.2): every global key of a
+// local row then comes from K_g, V_g (the window tiles drop global positions).
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [PP] "Sliding Window Attention: From Local Windows to Global Context"
@@ -104,6 +106,7 @@ __device__ inline uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t
 // Values the compiler cannot prove wave-uniform (they derive from blockIdx and
 // the wave index) are pinned to scalar registers.
 __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline uint32_t uni_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ inline const char *uni_ptr(const char *p) {
   const uint64_t v = (uint64_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -134,7 +137,7 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
         "global_load_lds_dwordx4 %6, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3])
+        : "s"(uni_u32(lds)), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3])
         : "scc");
   } else if constexpr (N == 1) {
     asm volatile(
@@ -143,7 +146,7 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
         "global_load_lds_dwordx4 %3, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]));
+        : "s"(uni_u32(lds)), "s"(uni_ptr(gbase)), "v"(off[0]));
   } else {
     static_assert(N == 2, "1, 2 or 4 copies per wave and tile");
     asm volatile(
@@ -154,7 +157,7 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
         "global_load_lds_dwordx4 %4, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(lds), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1])
+        : "s"(uni_u32(lds)), "s"(uni_ptr(gbase)), "v"(off[0]), "v"(off[1])
         : "scc");
   }
 }
@@ -169,7 +172,7 @@ __device__ inline void dma_dword(const char *gbase, uint32_t off, uint32_t lds) 
       "global_load_lds_dword %3, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "s"(uni_ptr(gbase)), "v"(off));
+      : "s"(uni_u32(lds)), "s"(uni_ptr(gbase)), "v"(off));
 }
 
 // Wait until at most n of this wave's vector-memory operations are still in
@@ -210,11 +213,12 @@ struct IntC {
 constexpr float kLazy = 8.f;
 
 // NW waves per workgroup; three waves per SIMD (12 per CU) bound the registers.
-// MODE: kCausal, kSymmetric, kRing or kCausalSink (FwdMode).
+// MODE: kCausal, kSymmetric, kRing, kCausalSink or kSymmetricProj (FwdMode).
 template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
     const FwdArgs a, const GlobalList gl) {
-  constexpr bool SYM = MODE == kSymmetric;
+  constexpr bool GPROJ = MODE == kSymmetricProj;  // separate global projections
+  constexpr bool SYM = MODE == kSymmetric || GPROJ;
   constexpr bool RING = MODE == kRing;
   constexpr bool CSINK = MODE == kCausalSink;  // causal with sink tokens / scores
   constexpr bool SCORE = CSINK || RING;        // may carry per-head sink scores
@@ -357,8 +361,20 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     const int p = lane % Gm::CPR;
     loff[t] = (uint32_t)(r * rs_b) + (p ^ (i >= Gm::NI ? swz_v<D>(r) : swz_k<D>(r))) * 16;
   }
+  // Copy sources as byte distances from the K base, so a copy picks its source
+  // by adding offsets (each choice between a distance and zero).  A choice
+  // between two captured pointer variables would be merged into one load
+  // through a selected capture address, which keeps every variable the
+  // lambdas capture in scratch memory.
   const char *kb8 = reinterpret_cast<const char *>(kbase);
-  const char *vb8 = reinterpret_cast<const char *>(vbase);
+  const long long d_v = (long long)((uintptr_t)vbase - (uintptr_t)kbase);  // V rows
+  // tiles of global keys read K_g, V_g with separate projections
+  const long long kv_off = ((long long)b * a.k_sb + (long long)kvh * a.k_sh) * 2;
+  const long long d_gk =
+      GPROJ ? (long long)((uintptr_t)a.kg + kv_off - (uintptr_t)kbase) : 0;
+  const long long d_gvk =  // (V_g - V) - (K_g - K)
+      GPROJ ? (long long)(((uintptr_t)a.vg - (uintptr_t)a.v) - ((uintptr_t)a.kg - (uintptr_t)a.k))
+            : 0;
   // DMA of the K and V rows of tile j (window tiles j < n_win, then tiles of
   // global keys) into the stage at LDS address `stage`.
   auto issue = [&](int j, uint32_t stage) {
@@ -370,7 +386,9 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       const int i = wave + t * NW;
       if (i < 2 * Gm::NI) {
         const bool isv = i >= Gm::NI;
-        const char *g8 = isv ? vb8 : kb8;
+        long long src = isv ? d_v : 0;
+        if (GPROJ && j >= n_win) src += d_gk + (isv ? d_gvk : 0);
+        const char *g8 = kb8 + src;
         const uint32_t ld = stage + (uint32_t)i * 1024u;
         if (whole) {
           // whole tile inside the class: uniform base + fixed lane offsets
@@ -509,6 +527,24 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       }
     }
   };
+  // Separate global projections: columns of window tile j holding a global
+  // position of this residue class (uniform; the loop runs over the globals).
+  auto glob_cols = [&](int j) -> uint64_t {
+    uint64_t m = 0;
+    if constexpr (GPROJ) {
+      if (j < n_win) {
+        const int c0 = (tr.lo + j) * BN;
+        for (int u = 0; u < a.G; ++u) {
+          const int d = gl.idx[b * a.G + u] - rho;
+          if (d >= 0 && d % dil == 0) {
+            const int c = d / dil - c0;
+            if (c >= 0 && c < BN) m |= 1ull << c;
+          }
+        }
+      }
+    }
+    return m;
+  };
   // every (valid row of this wave, key) pair of window tile j attended?
   auto tile_full = [&](int j) {
     if (j >= n_win) return false;  // tiles of global keys are always masked
@@ -573,12 +609,24 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   const int hi_key = min(SYM ? my_row + a.W : my_row, n_cls - 1);
   // mask of a partial tile: window predicate, or for a tile of global keys
   // the globals not already inside this row's (dilated) window
-  auto mask = [&](int j, f32x16 *sv) {
+  auto mask = [&](int j, f32x16 *sv, uint64_t gcols) {
     if (j < n_win) {
       // key of element (kb, e) = tile base + 4*lh + c(kb, e); compare c with
       // this lane's bounds shifted to the same origin
       const int base = (tr.lo + j) * BN + 4 * lh;
       const int lo = lo_key - base, hi = hi_key - base;
+      if (GPROJ && gcols) {
+        // global positions of this class in the tile go through K_g instead
+        const uint64_t gl_lane = gcols >> (4 * lh);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+            if (c < lo || c > hi || ((gl_lane >> c) & 1)) sv[kb][e] = -INFINITY;
+          }
+        return;
+      }
       if (CSINK && a.n_sink > 0 && tr.lo + j == 0) {
         // key tile 0 inside the window range: sinks s < n_sink, s <= t join
         const int hs = min(a.n_sink - 1, my_row) - base;
@@ -623,7 +671,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     uint64_t okb = 0;
     for (int c = 0; c < ng; ++c) {
       const int g = gl.idx[b * a.G + u0 + c];
-      if (!dilated_in(i_abs, g, a.W, dil)) okb |= 1ull << c;
+      if (GPROJ || !dilated_in(i_abs, g, a.W, dil)) okb |= 1ull << c;
     }
     okb >>= 4 * lh;  // this lane's columns are 4*lh + c(kb, e)
 #pragma unroll
@@ -659,7 +707,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       if constexpr (RING) {
         if (!ring_full(ks, j)) ring_mask(ks, j, sv);
       } else {
-        if (!tile_full(j)) mask(j, sv);
+        const uint64_t gcols = glob_cols(j);
+        if (gcols || !tile_full(j)) mask(j, sv, gcols);
       }
       rescale(rowmax(sv));
       exp_pack(sv, pu);
@@ -738,10 +787,11 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st) {
-  const int nblk = mode == kSymmetric ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
+  const bool sym = mode == kSymmetric || mode == kSymmetricProj;
+  const int nblk = sym ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
   if (nblk <= 0) return hipSuccess;
   constexpr int NWC = SWA_FWD_WAVES;
-  if (a.NW != (mode == kSymmetric ? 4 : NWC)) return hipErrorInvalidValue;
+  if (a.NW != (sym ? 4 : NWC)) return hipErrorInvalidValue;
   dim3 grid(nblk), block(64 * a.NW);
   if (mode == kCausal) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausal, NWC>), grid, block, 0, st, a, *gl);
@@ -752,6 +802,9 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *
   } else if (mode == kRing) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kRing, NWC>), grid, block, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_kernel<64, kRing, NWC>), grid, block, 0, st, a, *gl);
+  } else if (mode == kSymmetricProj) {
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kSymmetricProj, 4>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, kSymmetricProj, 4>), grid, block, 0, st, a, *gl);
   } else {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kSymmetric, 4>), grid, block, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_kernel<64, kSymmetric, 4>), grid, block, 0, st, a, *gl);

@@ -13,7 +13,10 @@
 // holding a position in (p-W, p] ([G3] "How it works").  Causal and ring
 // modes take attention sinks: the first n_sink positions stay visible ([KB] §4
 // "Failure mode 1"; [ST] "What's New") and a per-head sink score may join the
-// denominator.  Scores use the masked softmax of [KB] §2.
+// denominator.  With separate global projections ([PP] §5.2) a global row
+// reads q_g against k_g, v_g, and any other row reads every global key through
+// k_g, v_g and only the non-global window keys through k, v.  Scores use the
+// masked softmax of [KB] §2.
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com);
@@ -26,7 +29,8 @@ namespace {
 
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const GlobalList gl) {
-  constexpr bool SYM = MODE == kSymmetric;
+  constexpr bool GPROJ = MODE == kSymmetricProj;  // separate global projections
+  constexpr bool SYM = MODE == kSymmetric || GPROJ;
   constexpr bool RING = MODE == kRing;
   constexpr int DPL = D / 64;  // output columns per lane
   __shared__ float qs[4][D];
@@ -39,16 +43,29 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   const int b = live ? (int)(row_id / ((long long)a.T * a.Hq)) : 0;
   const int kvh = SYM ? h : h / a.group;
   const float *q = static_cast<const float *>(a.q);
-  const float *k = static_cast<const float *>(a.k) + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
-  const float *v = static_cast<const float *>(a.v) + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
+  const long long kv_off = (long long)b * a.k_sb + (long long)kvh * a.k_sh;
+  const float *k = static_cast<const float *>(a.k) + kv_off;
+  const float *v = static_cast<const float *>(a.v) + kv_off;
+  // keys and values of global positions (K_g, V_g, or the shared k, v)
+  const float *kgl = GPROJ ? static_cast<const float *>(a.kg) + kv_off : k;
+  const float *vgl = GPROJ ? static_cast<const float *>(a.vg) + kv_off : v;
+  bool is_glob = false;
+  if constexpr (SYM)
+    for (int g = 0; g < a.G; ++g) is_glob |= live && gl.idx[b * a.G + g] == t;
+  // a global row reads its query from Q_g and every key from K_g, V_g
+  if (GPROJ && is_glob) {
+    q = static_cast<const float *>(a.qg);
+    k = kgl;
+    v = vgl;
+  }
   for (int d = lane; d < D; d += 64)
     qs[wave][d] = live ? q[(long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D + d] : 0.f;
   __syncthreads();
   if (!live) return;
 
-  // Enumerate the connectivity set as idx -> key position (or -1 = skip).
+  // Enumerate the connectivity set as idx -> key position (or -1 = skip); a
+  // key at position p read through K_g, V_g is encoded as -2 - p.
   int n_keys, base = 0, kstep = 1, n_win = 0, n_sk = 0;
-  bool is_glob = false;
   const int dil = SYM ? a.dil[h] : 1;
   int my_pos = 0;
   if constexpr (RING) {
@@ -59,7 +76,6 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
     n_sk = min(a.n_sink, base);  // sink tokens before the window
     n_keys = n_sk + t - base + 1;
   } else {
-    for (int g = 0; g < a.G; ++g) is_glob |= gl.idx[b * a.G + g] == t;
     if (is_glob) {
       n_keys = a.T;
     } else {
@@ -86,15 +102,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
       } else if constexpr (!SYM) {
         key = (idx < n_sk) ? idx : base + (idx - n_sk);
       } else if (is_glob) key = base + idx * kstep;
-      else if (idx < n_win) key = base + idx * kstep;
-      else {
+      else if (idx < n_win) {
+        key = base + idx * kstep;
+        if constexpr (GPROJ)  // a global position is read through K_g below
+          for (int g = 0; g < a.G; ++g)
+            if (gl.idx[b * a.G + g] == key) key = -1;
+      } else {
         const int g = gl.idx[b * a.G + idx - n_win];
-        key = dilated_in(t, g, a.W, dil) ? -1 : g;  // already counted in the window
+        if constexpr (GPROJ) key = -2 - g;
+        else key = dilated_in(t, g, a.W, dil) ? -1 : g;  // already counted in the window
       }
     }
     float s = -INFINITY;
-    if (key >= 0) {
-      const float *kr = k + (long long)key * a.k_st;
+    if (key >= 0 || key <= -2) {
+      const float *kr = key >= 0 ? k + (long long)key * a.k_st : kgl + (long long)(-2 - key) * a.k_st;
       float dot = 0.f;
 #pragma unroll 8
       for (int d = 0; d < D; ++d) dot = fmaf(qs[wave][d], kr[d], dot);
@@ -118,8 +139,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
     for (int u = 0; u < cnt; ++u) {
       const float pu = __shfl(p, u);
       const int ku = __shfl(key, u);
-      if (ku >= 0) {
-        const float *vr = v + (long long)ku * a.k_st;
+      if (ku >= 0 || ku <= -2) {
+        const float *vr = ku >= 0 ? v + (long long)ku * a.k_st : vgl + (long long)(-2 - ku) * a.k_st;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pu, vr[lane + 64 * i], acc[i]);
       }
@@ -157,6 +178,9 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *g
   } else if (mode == kRing) {
     if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kRing>), g, blk, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_f32_kernel<64, kRing>), g, blk, 0, st, a, *gl);
+  } else if (mode == kSymmetricProj) {
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kSymmetricProj>), g, blk, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, kSymmetricProj>), g, blk, 0, st, a, *gl);
   } else {
     if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kSymmetric>), g, blk, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_f32_kernel<64, kSymmetric>), g, blk, 0, st, a, *gl);

@@ -300,13 +300,24 @@ size_t swa_longformer_workspace_size(int B, int T, int H, int d_h, int G) {
   return (size_t)B * H * G * S * (d_h + 2) * sizeof(float);
 }
 
-swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
-                          float *lse, int B, int T, int H, int d_h, int r, const int32_t *dilation,
-                          const int32_t *global_idx, int G, float scale, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace swa {
+namespace {
+
+// Longformer attention; qg, kg, vg null = the shared projections (swa_longformer),
+// else the separate global projections of swa_longformer_proj.
+swa_status longformer_impl(swa_dtype dt, const void *q, const void *k, const void *v,
+                           const void *qg, const void *kg, const void *vg, void *o, float *lse,
+                           int B, int T, int H, int d_h, int r, const int32_t *dilation,
+                           const int32_t *global_idx, int G, float scale, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   if (!dt_ok(dt) || !q || !k || !v || !o) return SWA_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  const bool proj = qg != nullptr;
+  if (proj && (!aligned(qg, 16) || !aligned(kg, 16) || !aligned(vg, 16)))
     return SWA_ERR_INVALID;
   if (B < 1 || T < 1 || H < 1 || r < 0 || G < 0 || !scale_ok(scale)) return SWA_ERR_INVALID;
   if ((G > 0) != (global_idx != nullptr)) return SWA_ERR_INVALID;
@@ -350,19 +361,29 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   if (tiles * B > 0x7fffffffLL || (dt == SWA_BF16 && a.k_sb * 2 >= (1LL << 31)))
     return SWA_ERR_UNSUPPORTED;
   a.tiles_per_batch = (int)tiles;
+  // With no global token the separate projections are never read.
+  const bool gproj = proj && G > 0;
+  if (gproj) {
+    a.qg = qg; a.kg = kg; a.vg = vg;
+  }
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
   for (int i = 0; i < B * G; ++i) gl.idx[i] = global_idx[i];
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, kSymmetric, d_h, &gl, st));
+  const int mode = gproj ? kSymmetricProj : kSymmetric;
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, mode, d_h, &gl, st));
 
-  hipError_t e = launch_fwd_bf16(a, kSymmetric, d_h, &gl, st);
+  hipError_t e = launch_fwd_bf16(a, mode, d_h, &gl, st);
   if (e != hipSuccess || G == 0) return hip_status(e);
   // Global rows attend every position: split-KV over all T keys, written after
-  // (stream order) the local pass, replacing those rows.
+  // (stream order) the local pass, replacing those rows.  With separate
+  // projections they read qg against kg, vg.
   SplitArgs s;
   std::memset(&s, 0, sizeof(s));
-  s.q = q; s.k = k; s.v = v; s.o = o; s.lse = lse;
+  s.q = gproj ? qg : q;
+  s.k = gproj ? kg : k;
+  s.v = gproj ? vg : v;
+  s.o = o; s.lse = lse;
   s.ws = static_cast<float *>(workspace);
   s.B = B; s.NKV = H; s.NQ = G;
   s.n_keys = T;
@@ -373,6 +394,30 @@ swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void
   s.k_sb = a.k_sb; s.k_sh = d_h; s.k_sr = a.k_st;
   s.sl2 = a.sl2;
   return hip_status(launch_split(s, false, false, d_h, &gl, G, H, st));
+}
+
+}  // namespace
+}  // namespace swa
+
+extern "C" {
+
+swa_status swa_longformer(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                          float *lse, int B, int T, int H, int d_h, int r, const int32_t *dilation,
+                          const int32_t *global_idx, int G, float scale, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return longformer_impl(dt, q, k, v, nullptr, nullptr, nullptr, o, lse, B, T, H, d_h, r,
+                         dilation, global_idx, G, scale, workspace, workspace_bytes, stream);
+}
+
+swa_status swa_longformer_proj(swa_dtype dt, const void *q, const void *k, const void *v,
+                               const void *qg, const void *kg, const void *vg, void *o,
+                               float *lse, int B, int T, int H, int d_h, int r,
+                               const int32_t *dilation, const int32_t *global_idx, int G,
+                               float scale, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  if (!qg || !kg || !vg) return SWA_ERR_INVALID;
+  return longformer_impl(dt, q, k, v, qg, kg, vg, o, lse, B, T, H, d_h, r, dilation, global_idx,
+                         G, scale, workspace, workspace_bytes, stream);
 }
 
 swa_status swa_debug_index_mask(int mode, int T, int w_or_r, int dil, const int32_t *global_idx,

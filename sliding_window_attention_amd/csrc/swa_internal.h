@@ -168,13 +168,16 @@ struct FwdArgs {
   // attention sinks (causal and ring modes)
   int n_sink;                // the first n_sink positions stay visible (<= kMaxSinks)
   const float *sink_logit;   // [H_q] per-head sink score in the denominator, or null
+  // symmetric mode: separate global projections (null = shared with q, k, v)
+  const void *qg, *kg, *vg;
 };
 
 constexpr int kMaxSinks = 32;  // sink tokens fit the first key tile
 
 // Window families of the banded kernels (kCausalSink: causal plus attention
 // sinks, a separate instantiation so the plain causal kernel carries none of it).
-enum FwdMode { kCausal = 0, kSymmetric = 1, kRing = 2, kCausalSink = 3 };
+// kSymmetricProj: symmetric with separate global projections.
+enum FwdMode { kCausal = 0, kSymmetric = 1, kRing = 2, kCausalSink = 3, kSymmetricProj = 4 };
 
 struct GlobalList {
   int idx[kMaxGlobalsLF];  // [B][G] positions

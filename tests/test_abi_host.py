@@ -107,6 +107,24 @@ def test_longformer_validation():
     assert bd.lib().swa_longformer_workspace_size(2, 64, 3, 64, 0) == 0
 
 
+def _lfp(qg=P, kg=P, vg=P, **kw):
+    a = dict(dt=0, B=2, T=64, H=3, D=64, r=4, sc=0.1, G=2)
+    a.update(kw)
+    gp = (ctypes.c_int32 * 4)(0, 8, 0, 8)
+    return bd.lib().swa_longformer_proj(a["dt"], P, P, P, qg, kg, vg, P, None, a["B"], a["T"],
+                                        a["H"], a["D"], a["r"], None, gp, a["G"], a["sc"], P,
+                                        1 << 30, S0)
+
+
+def test_longformer_proj_validation():
+    assert _lfp(qg=None) == INVALID
+    assert _lfp(kg=None) == INVALID
+    assert _lfp(vg=None) == INVALID
+    assert _lfp(kg=ctypes.c_void_p(4100)) == INVALID     # misaligned
+    assert _lfp(r=-1) == INVALID
+    assert _lfp(D=96) == UNSUPPORTED
+
+
 def test_cache_write_and_debug_validation():
     L = bd.lib()
     assert L.swa_cache_write(0, P, P, P, P, P, None, 1, 8, 1, 64, S0) == INVALID

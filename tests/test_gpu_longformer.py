@@ -58,6 +58,58 @@ def test_longformer_f32(case):
     assert max_err(lse, rl) <= TOL_LSE_F32
 
 
+# B, T, H, D, r, dilation, globals (separate global projections)
+PROJ = [
+    (1, 16, 2, 64, 2, [1, 2], [[0, 8]]),
+    (2, 300, 4, 64, 20, [1, 2, 3, 1], [[0, 77], [5, 299]]),
+    (2, 300, 2, 128, 20, [1, 2], [[10, 11], [0, 1]]),
+    (1, 129, 2, 128, 63, [4, 1], [[3, 64, 65, 100]]),
+    (2, 520, 4, 64, 64, [1, 1, 2, 2], [[0, 8], [200, 519]]),
+    (1, 200, 2, 64, 300, [1, 2], [[7]]),
+]
+
+
+def _run_proj(case, dtype):
+    B, T, H, D, r, dil, gl = case
+    c = inp.LongformerCase(B=B, T=T, H=H, D=D, r=r, dilation=dil, globals_=[], dtype=dtype,
+                           seed=3 * T + H)
+    q, k, v, dl, _ = inp.longformer_inputs(c)
+    # the global projections: independent seeded draws of the same shape
+    qg, kg, vg = (inp.as_io(inp.normal(q.shape, c.seed + 101 + i), dtype) for i in range(3))
+    g = np.asarray(gl, dtype=np.int32).reshape(B, -1)
+    banner(f"longformer_proj {dtype} {case}")
+    o, lse = bd.longformer(dev(q), dev(k), dev(v), r, dl, g, return_lse=True,
+                           qg=dev(qg), kg=dev(kg), vg=dev(vg))
+    torch.cuda.synchronize()
+    W = inp.widen
+    ro, rl = oracle.swa_longformer(W(q), W(k), W(v), r, dl, g, qg=W(qg), kg=W(kg), vg=W(vg))
+    return host(o), host(lse), ro, rl
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", PROJ, ids=[str(c[:5]) for c in PROJ])
+def test_longformer_separate_projections(case, dtype):
+    o, lse, ro, rl = _run_proj(case, dtype)
+    assert max_err(o, ro) <= (TOL_BF16 if dtype == "bf16" else TOL_F32)
+    assert max_err(lse, rl) <= (TOL_LSE_BF16 if dtype == "bf16" else TOL_LSE_F32)
+
+
+def test_longformer_proj_with_shared_tensors_is_longformer():
+    # qg, kg, vg = q, k, v must reproduce the shared-projection call exactly
+    # (the same arithmetic on the same operands).
+    c = inp.LongformerCase(B=2, T=300, H=4, D=64, r=20, dilation=[1, 2, 3, 1], globals_=[],
+                           dtype="bf16", seed=5)
+    q, k, v, dl, _ = inp.longformer_inputs(c)
+    g = np.asarray([[0, 77], [5, 299]], dtype=np.int32)
+    banner("longformer_proj shared == longformer")
+    a = bd.longformer(dev(q), dev(k), dev(v), c.r, dl, g)
+    b = bd.longformer(dev(q), dev(k), dev(v), c.r, dl, g, qg=dev(q), kg=dev(k), vg=dev(v))
+    torch.cuda.synchronize()
+    ro, _ = oracle.swa_longformer(inp.widen(q), inp.widen(k), inp.widen(v), c.r, dl, g)
+    assert max_err(host(b), ro) <= TOL_BF16
+    assert max_err(host(a), host(b)) <= 2 ** -7
+
+
 def test_small_symmetric_workload_fp32():
     # n=16, r=2, d_h=64, float32, one head: the running example's shape
     c = inp.C1
