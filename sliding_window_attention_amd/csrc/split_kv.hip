@@ -331,23 +331,36 @@ __device__ inline void dec_load_v(DecBlock<D> &blk, const uint16_t *vbase, const
   }
 }
 
-template <int D, int QG, bool DECODE>
-__global__ __launch_bounds__(64, QG >= 8 ? 1 : 2) void split_mfma_kernel(const SplitArgs a, const GlobalList gl,
-                                                        int G, int n_pass) {
+// NSW = 0: one wave per workgroup, workgroup x = split; the partial states go
+// to the workspace for combine_kernel.  NSW >= 1: the workgroup's NSW waves
+// are the splits of one (batch, kv head, query pass) and merge their partial
+// states in LDS at the end (no workspace, no second kernel).
+template <int D, int QG, bool DECODE, int NSW>
+__global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void split_mfma_kernel(
+    const SplitArgs a, const GlobalList gl, int G, int n_pass) {
   using Bk = DecBlock<D>;
   constexpr int KS = Bk::KS, TPR = Bk::TPR, RG = Bk::RG, RPL = Bk::RPL;
   constexpr int NPAIR = RPL / 2;
-  __shared__ uint32_t ppair[2][NPAIR][RG][QG];  // [parity][pair][row group][query]
+  constexpr int NWG = NSW > 0 ? NSW : 1;  // waves per workgroup
+  // [wave][parity][pair][row group][query]
+  __shared__ uint32_t ppair_all[NWG][2][NPAIR][RG][QG];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lq = lane & 31, lh = lane >> 5;
-  const int split = blockIdx.x;
+  const int split = NSW > 0 ? wave : blockIdx.x;
+  auto &ppair = ppair_all[wave];
   const int kvh = blockIdx.y / n_pass, q0 = (blockIdx.y % n_pass) * QG;
   const int b = blockIdx.z;
   const int nq = min(QG, a.NQ - q0);
-  const int c0 = split * a.chunk;
-  const int c1 = min(a.n_keys, c0 + a.chunk);
-  const int nblk = (c1 - c0 + 31) / 32;
+  // Keys of this wave: with NSW = 0 the split's chunk [c0, c1) in 32-key
+  // blocks; with NSW > 0 the waves interleave 32-key blocks (wave w takes
+  // blocks w, w + NSW, ...), so the workgroup reads K and V as two contiguous
+  // streams.  bstep = distance between a wave's consecutive blocks.
+  const int c0 = NSW > 0 ? 32 * wave : split * a.chunk;
+  const int c1 = NSW > 0 ? a.n_keys : min(a.n_keys, c0 + a.chunk);
+  constexpr int bstep = 32 * NWG;
+  const int nblk = NSW > 0 ? (c1 > c0 ? (c1 - c0 + bstep - 1) / bstep : 0) : (c1 - c0 + 31) / 32;
   int cur = 0;
   if constexpr (DECODE) cur = a.cur_pos[b];
 
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(64, QG >= 8 ? 1 : 2) void split_mfma_kernel(const S
   }
   for (int ib = 0; ib < nblk; ++ib) {
     const int parity = ib & 1;
-    const int s_next = c0 + 32 * (ib + 1);
+    const int s_next = c0 + (NSW > 0 ? bstep : 32) * (ib + 1);
     const bool more = ib + 1 < nblk;
     f32x16 s = f32x16{};
 #pragma unroll
@@ -438,7 +451,15 @@ __global__ __launch_bounds__(64, QG >= 8 ? 1 : 2) void split_mfma_kernel(const S
         }
       }
     }
-    __syncthreads();
+    // every lane reads the P values other lanes of this wave just wrote: LDS
+    // operations of one wave complete in order, so waiting for this wave's
+    // writes is enough (the other waves of the workgroup use their own slice)
+    if constexpr (NSW > 0) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      __syncthreads();
+    }
 #pragma unroll
     for (int q = 0; q < QG; ++q) {
       // alpha of query q lives in lane q
@@ -488,35 +509,99 @@ __global__ __launch_bounds__(64, QG >= 8 ? 1 : 2) void split_mfma_kernel(const S
       acc[q][e] = x;
     }
   const long long base = ((long long)b * a.NKV + kvh) * a.NQ;
-  if (lane < TPR) {
+  if constexpr (NSW == 0) {
+    if (lane < TPR) {
 #pragma unroll
-    for (int q = 0; q < QG; ++q) {
-      if (q < nq) {
-        float *dst = a.ws + ((base + q0 + q) * a.S + split) * (D + 2) + lane * 8;
+      for (int q = 0; q < QG; ++q) {
+        if (q < nq) {
+          float *dst = a.ws + ((base + q0 + q) * a.S + split) * (D + 2) + lane * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = acc[q][e];
+          for (int e = 0; e < 8; ++e) dst[e] = acc[q][e];
+        }
+      }
+    }
+    if (lh == 0 && lq < nq) {
+      float *dst = a.ws + ((base + q0 + lq) * a.S + split) * (D + 2);
+      dst[D] = m_run;
+      dst[D + 1] = l_run;
+    }
+  } else {
+    // Merge the NSW partial states of the workgroup, exactly as combine_kernel
+    // does across workgroups: with M = max_w m_w (log2 units),
+    // o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w.
+    __shared__ float m_acc[NSW][QG][D];
+    __shared__ float m_ml[NSW][QG][2];
+    if (lane < TPR) {
+#pragma unroll
+      for (int q = 0; q < QG; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m_acc[wave][q][lane * 8 + e] = acc[q][e];
+    }
+    if (lh == 0 && lq < QG) {
+      m_ml[wave][lq][0] = m_run;
+      m_ml[wave][lq][1] = l_run;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < QG * D; i += 64 * NSW) {
+      const int q = i / D, d = i % D;
+      if (q >= nq) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NSW; ++w) M = fmaxf(M, m_ml[w][q][0]);
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float L = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NSW; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(m_ml[w][q][0] - Mu);
+        L = fmaf(sc, m_ml[w][q][1], L);
+        o = fmaf(sc, m_acc[w][q][d], o);
+      }
+      o = (L > 0.f) ? o / L : 0.f;
+      long long row;
+      if constexpr (DECODE) row = b * a.o_sb + kvh * a.o_sh + (long long)(q0 + q) * a.o_sq;
+      else row = b * a.o_sb + kvh * a.o_sh + (long long)gl.idx[b * G + q0 + q] * a.o_sq;
+      const __bf16 hv = (__bf16)o;
+      static_cast<uint16_t *>(a.o)[row + d] = __builtin_bit_cast(uint16_t, hv);
+      if (a.lse && d == 0) {
+        const float lse = (L > 0.f) ? (M + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+        if constexpr (DECODE) a.lse[base + q0 + q] = lse;
+        else a.lse[((long long)b * a.NKV + kvh) * a.n_keys + gl.idx[b * G + q0 + q]] = lse;
       }
     }
   }
-  if (lh == 0 && lq < nq) {
-    float *dst = a.ws + ((base + q0 + lq) * a.S + split) * (D + 2);
-    dst[D] = m_run;
-    dst[D + 1] = l_run;
+}
+
+template <int D, int QG, bool DECODE>
+void launch_mfma_qg(const SplitArgs &a, const GlobalList *gl, int G, int n_pass, int nsw,
+                    hipStream_t st) {
+  if (nsw == 0) {
+    hipLaunchKernelGGL((split_mfma_kernel<D, QG, DECODE, 0>), dim3(a.S, a.NKV * n_pass, a.B),
+                       dim3(64), 0, st, a, *gl, G, n_pass);
+    return;
+  }
+  const dim3 grid(1, a.NKV * n_pass, a.B);
+  switch (nsw) {
+    case 1: hipLaunchKernelGGL((split_mfma_kernel<D, QG, DECODE, 1>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
+    case 2: hipLaunchKernelGGL((split_mfma_kernel<D, QG, DECODE, 2>), grid, dim3(128), 0, st, a, *gl, G, n_pass); break;
+    case 4: hipLaunchKernelGGL((split_mfma_kernel<D, QG, DECODE, 4>), grid, dim3(256), 0, st, a, *gl, G, n_pass); break;
+    default: hipLaunchKernelGGL((split_mfma_kernel<D, QG, DECODE, 8>), grid, dim3(512), 0, st, a, *gl, G, n_pass); break;
   }
 }
 
 template <int D, bool DECODE>
 hipError_t run_mfma(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) {
-  const int nq = a.NQ;
-  const int qg = nq >= 8 ? 8 : nq >= 4 ? 4 : nq >= 2 ? 2 : 1;
-  const int n_pass = (nq + qg - 1) / qg;
-  dim3 grid(a.S, a.NKV * n_pass, a.B);
+  const int qg = mfma_qg(a.NQ);
+  const int n_pass = (a.NQ + qg - 1) / qg;
+  // a.S in {1, 2, 4, 8} with a.merge set: the splits are the waves of one
+  // workgroup and merge in LDS; otherwise one workgroup per split + combine
+  const int nsw = a.merge ? a.S : 0;
   switch (qg) {
-    case 8: hipLaunchKernelGGL((split_mfma_kernel<D, 8, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
-    case 4: hipLaunchKernelGGL((split_mfma_kernel<D, 4, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
-    case 2: hipLaunchKernelGGL((split_mfma_kernel<D, 2, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
-    default: hipLaunchKernelGGL((split_mfma_kernel<D, 1, DECODE>), grid, dim3(64), 0, st, a, *gl, G, n_pass); break;
+    case 8: launch_mfma_qg<D, 8, DECODE>(a, gl, G, n_pass, nsw, st); break;
+    case 4: launch_mfma_qg<D, 4, DECODE>(a, gl, G, n_pass, nsw, st); break;
+    case 2: launch_mfma_qg<D, 2, DECODE>(a, gl, G, n_pass, nsw, st); break;
+    default: launch_mfma_qg<D, 1, DECODE>(a, gl, G, n_pass, nsw, st); break;
   }
+  if (a.merge) return hipGetLastError();
   hipLaunchKernelGGL((combine_kernel<D, false, DECODE>), dim3(a.NQ, a.NKV, a.B), dim3(D), 0, st, a,
                      *gl, G);
   return hipGetLastError();
@@ -590,6 +675,9 @@ hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const 
 }
 
 int split_max_chunk() { return kMaxChunk; }
+
+// Queries per pass of the bf16 split kernel (the query heads sharing a K/V head).
+int mfma_qg(int nq) { return nq >= 8 ? 8 : nq >= 4 ? 4 : nq >= 2 ? 2 : 1; }
 
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
                               void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,

@@ -250,6 +250,23 @@ swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const vo
   a.n_keys = W;
   a.S = splits_for(dt == SWA_F32, (long long)B * H_kv, W);
   a.chunk = chunk_for(dt == SWA_F32, W, a.S);
+  if (dt == SWA_BF16) {
+    // Enough (batch, kv head, query pass) groups: each workgroup takes one
+    // group, its waves split the ring and merge in LDS (no combine pass).
+    const int qg = mfma_qg(H_q / H_kv);
+    const long long groups = (long long)B * H_kv * ((H_q / H_kv + qg - 1) / qg);
+    for (int nsw = 1; nsw <= 8; nsw *= 2) {
+      if (groups * nsw >= SWA_STREAM_TARGET || nsw == 8) {
+        if (groups * nsw >= SWA_STREAM_TARGET / 2) {
+          a.merge = 1;
+          a.S = nsw;
+          a.chunk = (W + nsw - 1) / nsw;
+          a.chunk = (a.chunk + 31) / 32 * 32;
+        }
+        break;
+      }
+    }
+  }
   a.W = W;
   a.q_sq = d_h; a.q_sh = (long long)a.NQ * d_h; a.q_sb = (long long)H_q * d_h;
   a.o_sq = a.q_sq; a.o_sh = a.q_sh; a.o_sb = a.q_sb;

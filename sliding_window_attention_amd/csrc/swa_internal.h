@@ -198,6 +198,7 @@ struct SplitArgs {
   long long k_sb, k_sh, k_sr;     // k/v strides: batch, head, key row
   long long o_sb, o_sh, o_sq;     // o strides
   float sl2;
+  int merge;  // bf16: the S splits are the waves of one workgroup (S in {1, 2, 4, 8})
 };
 
 // ---------------------------------------------------------------- launchers (host)
@@ -208,6 +209,7 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *g
                           hipStream_t st);
 hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const GlobalList *gl,
                         int G, int H, hipStream_t st);
+int mfma_qg(int nq);  // queries per pass of the bf16 split kernel
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
                               void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,
                               int n_sink, hipStream_t st);

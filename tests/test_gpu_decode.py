@@ -37,6 +37,24 @@ def test_decode_full_ring(dtype, B, W, Hq, Hkv, D):
     _compare(q, kc, vc, sp, cur, W, dtype)
 
 
+# Batches with many (request, kv head) groups: the bf16 path then runs one
+# workgroup per group whose waves split the ring and merge in LDS (1, 2, 4 or
+# 8 waves by group count); cur_lo = 0 leaves some rings partly filled, and
+# W = 600 over 8 waves leaves the last wave an empty split.
+@pytest.mark.parametrize("B,W,Hq,Hkv,D,cur_lo", [
+    (256, 100, 16, 8, 128, 100),   # 2048 groups: one wave each
+    (128, 100, 8, 8, 128, 0),      # 1024 groups: two waves
+    (64, 700, 32, 8, 128, 0),      # 512 groups: four waves
+    (32, 600, 16, 4, 128, 300),    # 128 groups: eight waves, last split empty
+    (32, 600, 32, 4, 64, 0),       # eight query heads per kv head
+    (16, 333, 96, 8, 128, 0),      # twelve query heads per kv head: two passes
+])
+def test_decode_workgroup_merge(B, W, Hq, Hkv, D, cur_lo):
+    c = inp.DecodeCase(B=B, W=W, Hq=Hq, Hkv=Hkv, D=D, cur_lo=cur_lo, cur_hi=4 * W, seed=B + W + Hq)
+    q, kc, vc, sp, cur = inp.decode_inputs(c)
+    _compare(q, kc, vc, sp, cur, W, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_partial_stale_future_shuffled(dtype):
     B, W, Hq, Hkv, D = 6, 96, 8, 2, 128
