@@ -208,6 +208,11 @@ struct IntC {
   static constexpr int value = N;
 };
 
+// Copy stages of the symmetric (Longformer) kernel.
+#ifndef SWA_SYM_STAGES
+#define SWA_SYM_STAGES 2
+#endif
+
 // Largest growth (log2 units) of a row max tolerated before the running
 // reference max is raised and O, l are rescaled.
 constexpr float kLazy = 8.f;
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   // ring mode: the tile's slot positions follow its V tile (256 bytes)
   constexpr int SP_OFF = 2 * Gm::TILE_B;
   constexpr int STAGE_B = 2 * Gm::TILE_B + (RING ? 256 : 0);
-  constexpr int NST = 2;
+  constexpr int NST = SYM ? SWA_SYM_STAGES : 2;
   constexpr int OST_B = NW * kRowsPerWave * D * 2;
   constexpr int SMEM_B = (NST * STAGE_B > OST_B) ? NST * STAGE_B : OST_B;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_B];
