@@ -243,14 +243,14 @@ def main():
             workload="ring decode B=64 W=4096 Hq=32 Hkv=8 d_h=128 bf16, cur_pos in [4096, 32768)",
             value=round(r4["gbs"], 1), unit="GB/s", ms=round(r4["ms"], 4),
             frac_hbm_peak=round(r4["gbs"] / PEAK_HBM_GBS, 4), bytes=r4["bytes"],
-            traffic_split_pass=measured_traffic("split_mfma_kernel<128, 4, true>@262144"))
+            traffic=measured_traffic("split_mfma_kernel<128, 4, true, 4>@131072"))
     if args.only in ("all", "longformer"):
         r5 = bench_longformer(inp.C5, max(20, args.steps), args.warmup)
         extra["longformer"] = dict(
             workload="Longformer B=8 T=4096 H=12 d_h=64 r=256, dilation 2 on heads 8-11, globals {0,8}",
             value=round(r5["tflops"], 2), unit="TFLOP/s", ms=round(r5["ms"], 4),
             frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"],
-            traffic_local_pass=measured_traffic("fwd_kernel<64, true, 4>@786432"))
+            traffic_local_pass=measured_traffic("fwd_kernel<64, 1, 4>@786432"))
 
     if args.only in ("all", "chunk"):
         c6 = inp.C6
@@ -277,7 +277,7 @@ def main():
         cpu = cpu_baseline(c2)
 
     ach = main_r["tflops"]
-    tr = measured_traffic("fwd_kernel<128, false, 4>@1048576")
+    tr = measured_traffic("fwd_kernel<128, 0, 4>@1048576")
     out = {
         "metric": METRIC,
         "value": round(ach, 2),
@@ -298,7 +298,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if tr is None else tr["bytes"],
                      "traffic_detail": tr,
-                     "kernel": "fwd_kernel<128, causal>",
+                     "kernel": "fwd_kernel<128, 0 (causal), 4>",
                      "algorithmic_flop_per_launch": main_r["flops"],
                      "algorithmic_bytes_per_launch": main_r["bytes"]},
         "cpu_baseline": cpu,
