@@ -23,6 +23,7 @@ Modules
   attention   masked softmax attention over those sets (+ the dense-mask form)
   ring        the rolling-buffer KV cache write rule (one token or a chunk)
   tiles       brute-force band-tile classification for a (BM, BN) tiling
+  rope        rotary position embedding (rotate-half form) for the fused-RoPE variant
 
 Pins: every function here is pinned in ``tests/test_oracle_pins.py`` against the
 pages' printed tables and examples, closed forms, textbook special cases
@@ -34,6 +35,7 @@ beyond the special cases and invariants listed in the tests).
 
 from .index_sets import (
     causal_index_set,
+    causal_dilated_index_set,
     causal_sink_index_set,
     symmetric_index_set,
     longformer_index_set,
@@ -51,9 +53,12 @@ from .attention import (
 )
 from .ring import ring_write, ring_slot, ring_append, ring_from_sequence
 from .tiles import band_tiles_bruteforce
+from .rope import rope_rotate_half
 
 __all__ = [
     "causal_index_set",
+    "causal_dilated_index_set",
+    "rope_rotate_half",
     "symmetric_index_set",
     "longformer_index_set",
     "decode_index_set",

@@ -21,8 +21,9 @@ import math
 
 import numpy as np
 
-from .index_sets import (causal_index_set, causal_sink_index_set, decode_index_set,
-                         longformer_index_set)
+from .index_sets import (causal_dilated_index_set, causal_index_set, causal_sink_index_set,
+                         decode_index_set, longformer_index_set)
+from .rope import rope_rotate_half
 
 
 def _f64(x):
@@ -61,7 +62,8 @@ def _default_scale(d_h, scale):
     return 1.0 / math.sqrt(d_h) if scale is None else float(scale)
 
 
-def swa_prefill(q, k, v, W, scale=None, rows=None, n_sink=0, sink_logit=None):
+def swa_prefill(q, k, v, W, scale=None, rows=None, n_sink=0, sink_logit=None, dilation=None,
+                rope_base=None):
     """Causal sliding-window prefill with grouped-query heads.
 
     q: [B, T, H_q, d_h]; k, v: [B, T, H_kv, d_h]; query head h reads key/value
@@ -72,12 +74,23 @@ def swa_prefill(q, k, v, W, scale=None, rows=None, n_sink=0, sink_logit=None):
     ``n_sink`` > 0 adds the first n_sink positions to every window
     (``causal_sink_index_set``); ``sink_logit`` [H_q] gives each head a sink
     score in the denominator (see ``attend``).
+    ``dilation`` [H_q] (ints >= 1) gives head h the dilated window
+    {t - i*d_h : 0 <= i < W} of ``causal_dilated_index_set`` ([KB] §2 "Dilation").
+    ``rope_base``: q and k are first rotated by rotary position embeddings at
+    their token positions 0..T-1 (``rope.rope_rotate_half``; [G3] fixes the base
+    1e4 for local layers, [KB] §2 1e4 local / 1e6 global).
     Returns o [B, R, H_q, d_h] and lse [B, H_q, R] (R = len(rows) or T).
     """
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     if Hq % Hkv:
         raise ValueError("H_q must be a multiple of H_kv")
+    if n_sink and dilation is not None:
+        raise ValueError("sinks and dilation are separate variants")
+    if rope_base is not None:
+        pos = np.arange(T)
+        q = rope_rotate_half(q, pos, rope_base)
+        k = rope_rotate_half(k, pos, rope_base)
     group = Hq // Hkv
     sc = _default_scale(D, scale)
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -85,9 +98,13 @@ def swa_prefill(q, k, v, W, scale=None, rows=None, n_sink=0, sink_logit=None):
     lse = np.zeros((B, Hq, len(rows)), dtype=np.float64)
     for b in range(B):
         for ri, t in enumerate(rows):
-            S = causal_sink_index_set(int(t), W, n_sink) if n_sink else causal_index_set(int(t), W)
+            if n_sink:
+                S_all = causal_sink_index_set(int(t), W, n_sink)
+            elif dilation is None:
+                S_all = causal_index_set(int(t), W)
             for h in range(Hq):
                 kvh = h // group
+                S = S_all if dilation is None else causal_dilated_index_set(int(t), W, int(dilation[h]))
                 z = None if sink_logit is None else sink_logit[h]
                 o[b, ri, h], lse[b, h, ri] = attend(q[b, t, h], k[b, S, kvh], v[b, S, kvh], sc, z)
     return o, lse

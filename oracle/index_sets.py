@@ -21,6 +21,21 @@ def causal_index_set(t: int, W: int) -> np.ndarray:
     return np.arange(max(0, t - W + 1), t + 1, dtype=np.int64)
 
 
+def causal_dilated_index_set(t: int, W: int, dilation: int = 1) -> np.ndarray:
+    """Dilated causal window: keys t - i*d for 0 <= i < W that are >= 0.
+
+    [KB] §2 "Dilation": the window N_t is replaced by {t - i*d : 0 <= i < W}
+    with gap d >= 1 (heads may use different d).  Positions below 0 do not
+    exist, so the set is cut there, as the undilated window is (a reading: the
+    page does not spell out the start of the sequence).  d = 1 is the causal
+    window of ``causal_index_set``.
+    """
+    if W < 1 or dilation < 1:
+        raise ValueError("need W >= 1 and dilation >= 1")
+    keys = [t - i * dilation for i in range(W) if t - i * dilation >= 0]
+    return np.asarray(sorted(keys), dtype=np.int64)
+
+
 def symmetric_index_set(i: int, n: int, r: int, dilation: int = 1) -> np.ndarray:
     """Symmetric (encoder) window with optional dilation, clipped to [0, n-1].
 

@@ -514,6 +514,111 @@ def test_global_projections_against_sdpa_on_stacked_keys():
 
 # ---------------------------------------------------------------- tiles
 
+# ---------------------------------------------------------------- causal dilation ([KB] §2 "Dilation")
+
+def test_causal_dilated_set_by_definition_and_count():
+    # {t - i*d : 0 <= i < W} cut at 0: brute force over a grid of positions
+    for d in (1, 2, 3, 7):
+        for W in (1, 2, 5, 40):
+            for t in range(0, 60):
+                want = sorted(x for x in range(0, t + 1) if (t - x) % d == 0 and (t - x) // d < W)
+                got = oracle.causal_dilated_index_set(t, W, d).tolist()
+                assert got == want
+                assert len(got) == min(W, t // d + 1)
+    # d = 1 is the plain causal window
+    for t in range(30):
+        assert oracle.causal_dilated_index_set(t, 7, 1).tolist() == oracle.causal_index_set(t, 7).tolist()
+
+
+def test_causal_dilated_is_residue_class_problem():
+    # a dilated head is d independent causal problems on the subsequences
+    # x[rho::d]: the window of t is rho + d * (causal window of t // d)
+    for d in (2, 3, 5):
+        for W in (1, 4, 9):
+            for t in range(50):
+                rho, i = t % d, t // d
+                cls = rho + d * oracle.causal_index_set(i, W)
+                assert oracle.causal_dilated_index_set(t, W, d).tolist() == cls.tolist()
+
+
+def test_causal_dilated_attention_against_sdpa_per_class():
+    # per residue class with a window covering the class, dilated SWA is dense
+    # causal attention on that class subsequence (torch SDPA, float64)
+    B, T, Hq, Hkv, D = 2, 23, 4, 2, 8
+    q, k, v = _rand((B, T, Hq, D), 61), _rand((B, T, Hkv, D), 62), _rand((B, T, Hkv, D), 63)
+    dil = [1, 3, 2, 3]
+    o, _ = oracle.swa_prefill(q, k, v, T, dilation=dil)
+    for h, d in enumerate(dil):
+        kvh = h // (Hq // Hkv)
+        for rho in range(d):
+            sl = slice(rho, None, d)
+            want = _sdpa(q[:, sl, h:h + 1], k[:, sl, kvh:kvh + 1], v[:, sl, kvh:kvh + 1], True,
+                         scale=1 / math.sqrt(D))
+            np.testing.assert_allclose(o[:, sl, h:h + 1], want, rtol=0, atol=1e-12)
+
+
+def test_causal_dilated_zero_query_is_mean_over_dilated_window():
+    B, T, H, D, W = 1, 40, 2, 4, 5
+    q = np.zeros((B, T, H, D))
+    k, v = _rand((B, T, H, D), 64), _rand((B, T, H, D), 65)
+    o, _ = oracle.swa_prefill(q, k, v, W, dilation=[2, 4])
+    for h, d in enumerate((2, 4)):
+        for t in range(T):
+            keys = [t - i * d for i in range(W) if t - i * d >= 0]
+            np.testing.assert_allclose(o[0, t, h], v[0, keys, h].mean(axis=0), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- rotary positions ([G3], [KB] §2)
+
+def test_rope_is_complex_rotation():
+    # the rotate-half pair (x_i, x_{i+d/2}) as the complex number x_i + j x_{i+d/2},
+    # multiplied by exp(j p theta_i), theta_i = base^(-2i/d)
+    T, H, D, base = 9, 3, 16, 1.0e4
+    x = _rand((T, H, D), 66)
+    pos = np.array([0, 1, 2, 5, 100, 4095, 16383, 32767, 70000])
+    r = oracle.rope_rotate_half(x, pos, base)
+    z = x[..., :D // 2] + 1j * x[..., D // 2:]
+    th = base ** (-np.arange(D // 2) * 2.0 / D)
+    zr = z * np.exp(1j * pos[:, None, None] * th[None, None, :])
+    np.testing.assert_allclose(r[..., :D // 2], zr.real, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(r[..., D // 2:], zr.imag, rtol=0, atol=1e-9)
+
+
+def test_rope_position_zero_identity_norms_and_relative_phase():
+    T, H, D = 12, 2, 8
+    x = _rand((1, T, H, D), 67)
+    y = _rand((1, T, H, D), 68)
+    pos = np.arange(T)
+    rx = oracle.rope_rotate_half(x, pos, 1.0e6)
+    ry = oracle.rope_rotate_half(y, pos, 1.0e6)
+    np.testing.assert_array_equal(rx[:, 0], x[:, 0])                        # p = 0: no rotation
+    np.testing.assert_allclose(np.linalg.norm(rx, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    # q_m . k_n depends on m - n only: shift both positions by 37
+    sx = oracle.rope_rotate_half(x, pos + 37, 1.0e6)
+    sy = oracle.rope_rotate_half(y, pos + 37, 1.0e6)
+    for m in range(T):
+        for n in range(T):
+            a = rx[0, m, 0] @ ry[0, n, 0]
+            b = sx[0, m, 0] @ sy[0, n, 0]
+            assert abs(a - b) < 1e-11
+
+
+def test_prefill_with_rope_equals_prefill_of_rotated_inputs():
+    # the rope_base option is exactly "rotate q and k at their positions, then attend"
+    B, T, Hq, Hkv, D, W = 1, 17, 2, 1, 8, 6
+    q, k, v = _rand((B, T, Hq, D), 69), _rand((B, T, Hkv, D), 70), _rand((B, T, Hkv, D), 71)
+    z = q[..., :D // 2] + 1j * q[..., D // 2:]
+    th = 1.0e4 ** (-np.arange(D // 2) * 2.0 / D)
+    ph = np.exp(1j * np.arange(T)[None, :, None, None] * th)
+    qr = np.concatenate([(z * ph).real, (z * ph).imag], axis=-1)
+    zk = k[..., :D // 2] + 1j * k[..., D // 2:]
+    kr = np.concatenate([(zk * ph).real, (zk * ph).imag], axis=-1)
+    o1, l1 = oracle.swa_prefill(q, k, v, W, rope_base=1.0e4)
+    o2, l2 = oracle.swa_prefill(qr, kr, v, W)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
 def test_tiles_hand_example():
     # T=16, W=4, BM=BN=4 (causal): block 0 sees only the diagonal block; later
     # blocks see their diagonal block and the one before, both partly masked.
