@@ -9,6 +9,8 @@
  * of "Sliding Window Attention: From Local Windows to Global Context"
  * (prathamp.com)).  The entry points differ only in S_t:
  *   swa_prefill     causal window  t-W < s <= t                (knowledge base §2, §3)
+ *   swa_prefill_dilated  causal windows {t - i*d : 0 <= i < W} with a dilation
+ *                   per head (knowledge base §2 "Dilation")
  *   swa_prefill_sinks  the causal window plus pinned sink tokens and an optional
  *                   per-head sink score (knowledge base §4; superteams.ai "What's New")
  *   swa_decode      ring cache of W slots, window from stored absolute positions
@@ -90,6 +92,19 @@ swa_status swa_prefill(swa_dtype dt, const void *q, const void *k, const void *v
 swa_status swa_prefill_sinks(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
                              float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
                              int n_sink, const float *sink_logit, float scale, void *stream);
+
+/* Causal prefill with dilated windows.  Query t of head h attends the keys
+ * t - i*d for 0 <= i < W that are >= 0, d = dilation[h] (knowledge base §2
+ * "Dilation": the window {t - i*d : 0 <= i < W}, heads may use different d).
+ * The key/value head of query head h is h / (H_q / H_kv) as in swa_prefill.
+ *   dilation : HOST int32 [H_q], each in [1, 65535], or NULL (= all 1, which is
+ *              swa_prefill); H_q <= 256 when some dilation is not 1
+ * Arguments otherwise as swa_prefill.
+ * Errors: as swa_prefill, plus INVALID for a dilation outside [1, 65535] and
+ * UNSUPPORTED for more than 256 query heads with dilation. */
+swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                               float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                               const int32_t *dilation, float scale, void *stream);
 
 /* Decode over a rolling-buffer KV cache: one new query token per request.
  * Token p is stored in slot p mod W (knowledge base §2 "KV cache"); every slot

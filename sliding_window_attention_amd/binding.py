@@ -45,6 +45,7 @@ def lib():
         L.swa_prefill_cached.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
                                          vp, f, vp]
         L.swa_prefill_sinks.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, f, vp]
+        L.swa_prefill_dilated.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, f, vp]
         L.swa_longformer_workspace_size.argtypes = [i, i, i, i, i]
         L.swa_longformer_workspace_size.restype = sz
         L.swa_longformer.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, f, vp, sz, vp]
@@ -55,7 +56,8 @@ def lib():
         L.swa_debug_index_mask.argtypes = [i, i, i, i, vp, i, vp, vp]
         L.swa_status_str.argtypes = [i]
         L.swa_status_str.restype = ctypes.c_char_p
-        for name in ("swa_prefill", "swa_prefill_sinks", "swa_prefill_cached", "swa_decode",
+        for name in ("swa_prefill", "swa_prefill_sinks", "swa_prefill_dilated",
+                     "swa_prefill_cached", "swa_decode",
                      "swa_cache_write", "swa_cache_append", "swa_longformer",
                      "swa_longformer_proj", "swa_tile_config", "swa_debug_index_mask"):
             getattr(L, name).restype = i
@@ -125,6 +127,27 @@ def prefill_sinks(q, k, v, W, n_sink=0, sink_logit=None, scale=None, out=None,
     _check(lib().swa_prefill_sinks(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq,
                                    Hkv, D, int(W), int(n_sink), _ptr(sink_logit), sc, _stream(q)),
            "swa_prefill_sinks")
+    return (o, lse) if return_lse else o
+
+
+def prefill_dilated(q, k, v, W, dilation=None, scale=None, out=None, return_lse=False):
+    """Causal windows {t - i*d : 0 <= i < W} with d = dilation[h] per query head
+    (host int sequence [Hq] or None = all 1)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dil = None
+    if dilation is not None:
+        if len(dilation) != Hq:
+            raise ValueError("dilation needs one entry per query head")
+        dil = (ctypes.c_int32 * Hq)(*[int(x) for x in dilation])
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(B, Hq, T, device=q.device, dtype=torch.float32) if return_lse else None
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().swa_prefill_dilated(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T,
+                                     Hq, Hkv, D, int(W), dil, sc, _stream(q)),
+           "swa_prefill_dilated")
     return (o, lse) if return_lse else o
 
 

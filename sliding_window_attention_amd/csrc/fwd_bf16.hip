@@ -28,6 +28,9 @@
 // mode, a chunk of queries with absolute positions against the slots of a ring
 // cache, slot attended iff its stored position p has q_pos-W < p <= q_pos
 // ([G3] "How it works": the window comes from positions, not buffer offsets).
+// Dilated causal heads ([KB] §2 "Dilation": window {t - i*d : 0 <= i < W})
+// run the causal window inside each residue class t mod d, as symmetric mode
+// does for dilated Longformer heads.
 // Causal and ring modes take attention sinks: the first n_sink positions stay
 // visible next to the window ([KB] §4 "Failure mode 1"; [ST] "What's New"), and
 // an optional per-head sink score joins the softmax denominator.  Symmetric
@@ -226,6 +229,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   constexpr bool SYM = MODE == kSymmetric || GPROJ;
   constexpr bool RING = MODE == kRing;
   constexpr bool CSINK = MODE == kCausalSink;  // causal with sink tokens / scores
+  constexpr bool CDIL = MODE == kCausalDil;    // causal, dilated heads (residue classes)
   constexpr bool SCORE = CSINK || RING;        // may carry per-head sink scores
   using Gm = Geo<D>;
   // NST stages, each a row-major K tile followed by a V tile (swizzled
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   int b, h, kvh, row0;  // row0: first query row (class index in symmetric mode)
   int rho = 0, dil = 1, n_cls;  // residue class, dilation, class length
   int tile_row0, tile_rows;     // workgroup's query rows (for the tile schedule)
-  if constexpr (!SYM) {
+  if constexpr (!SYM && !CDIL) {
     const int nblk = a.B * a.n_hg * a.n_qt;
     const int lid = xcd_remap(blockIdx.x, nblk);
     const int qt = a.n_qt - 1 - (lid % a.n_qt);  // heavy (full-band) tiles first
@@ -267,23 +271,32 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     row0 = tile_row0 + (wave / a.P) * kRowsPerWave;
     n_cls = a.T;
   } else {
+    // (batch, head or head group, residue class, query tile); in a dilated
+    // causal head group the waves take P heads x NW/P row blocks as above
     const int nblk = a.B * a.tiles_per_batch;
     const int lid = xcd_remap(blockIdx.x, nblk);
     b = lid / a.tiles_per_batch;
     const int rem = lid % a.tiles_per_batch;
-    int lo = 0, hi = a.Hq - 1;  // find head: head_off[h] <= rem < head_off[h+1]
+    // find the head (group): head_off[g] <= rem < head_off[g+1]
+    int lo = 0, hi = (SYM ? a.Hq : a.n_hg) - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (a.head_off[mid] <= rem) lo = mid; else hi = mid - 1;
     }
-    h = lo;
-    kvh = h;
-    dil = a.dil[h];
+    dil = a.dil[lo];
     int tile;
-    class_tile_decode(a.T, dil, a.BM, rem - a.head_off[h], &rho, &tile);
+    class_tile_decode(a.T, dil, a.BM, rem - a.head_off[lo], &rho, &tile);
     n_cls = class_len(class_split(a.T, dil), rho);
     tile_row0 = tile * a.BM;
-    row0 = tile_row0 + wave * kRowsPerWave;
+    if constexpr (SYM) {
+      h = lo;
+      kvh = h;
+      row0 = tile_row0 + wave * kRowsPerWave;
+    } else {
+      h = lo * a.P + (wave % a.P);
+      kvh = h / a.group;
+      row0 = tile_row0 + (wave / a.P) * kRowsPerWave;
+    }
   }
   b = uni(b);
   h = uni(h);
@@ -793,7 +806,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
 hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st) {
   const bool sym = mode == kSymmetric || mode == kSymmetricProj;
-  const int nblk = sym ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
+  const int nblk = (sym || mode == kCausalDil) ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
   if (nblk <= 0) return hipSuccess;
   constexpr int NWC = SWA_FWD_WAVES;
   if (a.NW != (sym ? 4 : NWC)) return hipErrorInvalidValue;
@@ -810,6 +823,9 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *
   } else if (mode == kSymmetricProj) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kSymmetricProj, 4>), grid, block, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_kernel<64, kSymmetricProj, 4>), grid, block, 0, st, a, *gl);
+  } else if (mode == kCausalDil) {
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausalDil, NWC>), grid, block, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_kernel<64, kCausalDil, NWC>), grid, block, 0, st, a, *gl);
   } else {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kSymmetric, 4>), grid, block, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_kernel<64, kSymmetric, 4>), grid, block, 0, st, a, *gl);

@@ -13,7 +13,8 @@
 // holding a position in (p-W, p] ([G3] "How it works").  Causal and ring
 // modes take attention sinks: the first n_sink positions stay visible ([KB] §4
 // "Failure mode 1"; [ST] "What's New") and a per-head sink score may join the
-// denominator.  With separate global projections ([PP] §5.2) a global row
+// denominator.  Dilated causal heads ([KB] §2 "Dilation") attend
+// {t - i*d : 0 <= i < W}, cut at 0.  With separate global projections ([PP] §5.2) a global row
 // reads q_g against k_g, v_g, and any other row reads every global key through
 // k_g, v_g and only the non-global window keys through k, v.  Scores use the
 // masked softmax of [KB] §2.
@@ -32,6 +33,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   constexpr bool GPROJ = MODE == kSymmetricProj;  // separate global projections
   constexpr bool SYM = MODE == kSymmetric || GPROJ;
   constexpr bool RING = MODE == kRing;
+  constexpr bool CDIL = MODE == kCausalDil;  // dilated causal: a.dil[h] per query head
   constexpr int DPL = D / 64;  // output columns per lane
   __shared__ float qs[4][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -71,6 +73,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   if constexpr (RING) {
     n_keys = a.S;  // every slot; the position test below picks the window
     my_pos = a.q_pos[(long long)b * a.T + t];
+  } else if constexpr (CDIL) {
+    kstep = a.dil[h];
+    n_keys = min(a.W, t / kstep + 1);  // keys t, t - d, ..., >= 0
   } else if constexpr (!SYM) {
     base = max(0, t - a.W + 1);
     n_sk = min(a.n_sink, base);  // sink tokens before the window
@@ -99,6 +104,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
       if constexpr (RING) {
         const int p = a.slot_pos[(long long)b * a.S + idx];
         key = (p >= 0 && p <= my_pos && (p > my_pos - a.W || p < a.n_sink)) ? idx : -1;
+      } else if constexpr (CDIL) {
+        key = t - idx * kstep;
       } else if constexpr (!SYM) {
         key = (idx < n_sk) ? idx : base + (idx - n_sk);
       } else if (is_glob) key = base + idx * kstep;
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
   }
   float inv = (l > 0.f) ? 1.f / l : 0.f;
   float lse2 = (l > 0.f) ? m + log2f(l) : -INFINITY;  // log2 units
-  if (!SYM && a.sink_logit) {
+  if (!SYM && !CDIL && a.sink_logit) {
     // the sink score z joins the denominator: 2^(z log2 e - m) against max(m, z)
     const float z2 = a.sink_logit[h] * 1.4426950408889634f;
     const float mu = (m == -INFINITY) ? z2 : fmaxf(m, z2);
@@ -178,6 +185,9 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *g
   } else if (mode == kRing) {
     if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kRing>), g, blk, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_f32_kernel<64, kRing>), g, blk, 0, st, a, *gl);
+  } else if (mode == kCausalDil) {
+    if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kCausalDil>), g, blk, 0, st, a, *gl);
+    else hipLaunchKernelGGL((fwd_f32_kernel<64, kCausalDil>), g, blk, 0, st, a, *gl);
   } else if (mode == kSymmetricProj) {
     if (D == 128) hipLaunchKernelGGL((fwd_f32_kernel<128, kSymmetricProj>), g, blk, 0, st, a, *gl);
     else hipLaunchKernelGGL((fwd_f32_kernel<64, kSymmetricProj>), g, blk, 0, st, a, *gl);

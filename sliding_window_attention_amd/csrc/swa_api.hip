@@ -172,6 +172,67 @@ swa_status swa_prefill_sinks(swa_dtype dt, const void *q, const void *k, const v
   return hip_status(launch_fwd_bf16(a, mode, d_h, &gl, st));
 }
 
+swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                               float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                               const int32_t *dilation, float scale, void *stream) {
+  if (!dt_ok(dt) || !q || !k || !v || !o) return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || T < 1 || H_q < 1 || H_kv < 1 || W < 1 || H_q % H_kv || !scale_ok(scale))
+    return SWA_ERR_INVALID;
+  if (dilation)
+    for (int h = 0; h < H_q; ++h)
+      if (dilation[h] < 1 || dilation[h] > 65535) return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  bool any = false;
+  for (int h = 0; dilation && h < H_q; ++h) any |= dilation[h] != 1;
+  if (!any)
+    return swa_prefill(dt, q, k, v, o, lse, B, T, H_q, H_kv, d_h, W, scale, stream);
+
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.T = T; a.Hq = H_q; a.Hkv = H_kv;
+  a.q_st = (long long)H_q * d_h;
+  a.q_sb = a.q_st * T;
+  a.k_st = (long long)H_kv * d_h;
+  a.k_sb = a.k_st * T;
+  a.k_sh = d_h;
+  a.W = W;
+  a.sl2 = scale * kLog2e;
+  a.group = H_q / H_kv;
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == SWA_F32) {
+    if (H_q > kMaxHeadsLF) return SWA_ERR_UNSUPPORTED;
+    for (int h = 0; h < H_q; ++h) a.dil[h] = (unsigned short)dilation[h];
+    return hip_status(launch_fwd_f32(a, kCausalDil, d_h, &gl, st));
+  }
+  // Heads packed into one workgroup share their key/value head; they must
+  // share the dilation too, else one head per workgroup.
+  int P = prefill_pack(H_q, H_kv);
+  for (int h = 0; h < H_q && P > 1; ++h)
+    if (dilation[h] != dilation[h - h % P]) P = 1;
+  a.P = P;
+  a.NW = fwd_waves(false);
+  a.BM = kRowsPerWave * a.NW / P;
+  a.n_hg = H_q / P;
+  if (a.n_hg > kMaxHeadsLF) return SWA_ERR_UNSUPPORTED;
+  long long tiles = 0;
+  for (int g = 0; g < a.n_hg; ++g) {
+    a.dil[g] = (unsigned short)dilation[g * P];
+    a.head_off[g] = (int)tiles;
+    tiles += class_tiles(T, a.dil[g], a.BM);
+  }
+  a.head_off[a.n_hg] = (int)tiles;
+  // bf16 kernels address one batch slice of K/V with 32-bit byte offsets
+  if (tiles * B > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31)) return SWA_ERR_UNSUPPORTED;
+  a.tiles_per_batch = (int)tiles;
+  return hip_status(launch_fwd_bf16(a, kCausalDil, d_h, &gl, st));
+}
+
 swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
                               const void *v_cache, const int32_t *slot_pos, const int32_t *q_pos,
                               void *o, float *lse, int B, int L, int S, int H_q, int H_kv,

@@ -156,11 +156,13 @@ struct FwdArgs {
   int n_qt, n_hg;        // causal: query tiles per head group, head groups
   int BM;                // query rows per workgroup
   int NW;                // waves per workgroup
-  // symmetric (Longformer) mode
+  // symmetric (Longformer) and dilated causal modes: work is enumerated per
+  // head (symmetric) or head group of P heads (dilated causal), residue class
+  // and query tile
   int G;                       // globals per batch row
-  int tiles_per_batch;         // sum over heads of class tiles
-  int head_off[kMaxHeadsLF + 1];   // prefix sums of class tiles per head
-  unsigned short dil[kMaxHeadsLF]; // per-head dilation
+  int tiles_per_batch;         // sum over heads / head groups of class tiles
+  int head_off[kMaxHeadsLF + 1];   // prefix sums of class tiles per head (group)
+  unsigned short dil[kMaxHeadsLF]; // dilation per head (group)
   // ring mode (a chunk of queries over a ring cache)
   const int *slot_pos;   // [B, S] position held by each slot (< 0 = empty)
   const int *q_pos;      // [B, T] absolute position of each query row
@@ -176,8 +178,16 @@ constexpr int kMaxSinks = 32;  // sink tokens fit the first key tile
 
 // Window families of the banded kernels (kCausalSink: causal plus attention
 // sinks, a separate instantiation so the plain causal kernel carries none of it).
-// kSymmetricProj: symmetric with separate global projections.
-enum FwdMode { kCausal = 0, kSymmetric = 1, kRing = 2, kCausalSink = 3, kSymmetricProj = 4 };
+// kSymmetricProj: symmetric with separate global projections.  kCausalDil:
+// causal with a dilation per head group (residue classes, like symmetric mode).
+enum FwdMode {
+  kCausal = 0,
+  kSymmetric = 1,
+  kRing = 2,
+  kCausalSink = 3,
+  kSymmetricProj = 4,
+  kCausalDil = 5
+};
 
 struct GlobalList {
   int idx[kMaxGlobalsLF];  // [B][G] positions

@@ -116,6 +116,21 @@ def _lfp(qg=P, kg=P, vg=P, **kw):
                                         1 << 30, S0)
 
 
+def test_prefill_dilated_validation():
+    L = bd.lib()
+
+    def call(dil, Hq=4, Hkv=2, D=128, W=8):
+        dp = None if dil is None else (ctypes.c_int32 * len(dil))(*dil)
+        return L.swa_prefill_dilated(0, P, P, P, P, None, 1, 16, Hq, Hkv, D, W, dp, 0.1, S0)
+
+    assert call([1, 0, 2, 2]) == INVALID
+    assert call([1, 70000, 2, 2]) == INVALID
+    assert call([1, 2, 2, 2], W=0) == INVALID
+    assert call([1, 2, 2, 2], Hq=3, Hkv=2) == INVALID
+    assert call([1, 2, 2, 2], D=96) == UNSUPPORTED
+    assert call([1, 2] * 150, Hq=300, Hkv=1) == UNSUPPORTED  # 300 single-head groups
+
+
 def test_longformer_proj_validation():
     assert _lfp(qg=None) == INVALID
     assert _lfp(kg=None) == INVALID
