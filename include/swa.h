@@ -106,6 +106,36 @@ swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const
                                float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
                                const int32_t *dilation, float scale, void *stream);
 
+/* Rotary position embedding, rotate-half form: for a token at position p the
+ * pair (x_i, x_{i + d_h/2}) of every head turns by the angle p * base^(-2i/d_h):
+ *   x_i' = x_i cos - x_{i+d/2} sin,   x_{i+d/2}' = x_{i+d/2} cos + x_i sin.
+ * The Gemma 3 note ("How it works") keeps base 1e4 on local sliding-window
+ * layers; the knowledge base (§2 "Interleaved local/global schemes") gives 1e4
+ * local / 1e6 global.  The pairing is the common rotate-half convention.
+ *   x, y : [B, T, H, d_h] device (y may equal x: in place)
+ *   pos  : device int32 [B, T] positions, or NULL for p = t
+ * Errors: INVALID for null or misaligned pointers, B, T, H < 1, a base that is
+ * not finite and > 0; UNSUPPORTED for other d_h. */
+swa_status swa_rope(swa_dtype dt, const void *x, void *y, const int32_t *pos, int B, int T, int H,
+                    int d_h, float rope_base, void *stream);
+
+/* Causal prefill with rotary positions applied to q and k first (positions
+ * 0..T-1, base rope_base): the result is swa_prefill(rope(q), rope(k), v).
+ * The queries are rotated in registers inside the prefill kernel; the keys are
+ * rotated once into the workspace (every key feeds W / 32 query tiles, so
+ * rotating inside the banded loop would repeat the work that often); q and k
+ * are not modified.  The rotated values enter the MFMA products rounded to
+ * bf16 (bf16 path).
+ *   workspace : device scratch of at least swa_prefill_rope_workspace_size()
+ *               bytes (the rotated keys, [B, T, H_kv, d_h]), 16-byte aligned.
+ * Arguments otherwise as swa_prefill.  Errors: as swa_prefill, plus INVALID
+ * for a bad base and WORKSPACE for a small workspace. */
+size_t swa_prefill_rope_workspace_size(swa_dtype dt, int B, int T, int H_kv, int d_h);
+swa_status swa_prefill_rope(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                            float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                            float rope_base, float scale, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* Decode over a rolling-buffer KV cache: one new query token per request.
  * Token p is stored in slot p mod W (knowledge base §2 "KV cache"); every slot
  * records the absolute position it holds, and the window is computed from those

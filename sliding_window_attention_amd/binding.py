@@ -46,6 +46,10 @@ def lib():
                                          vp, f, vp]
         L.swa_prefill_sinks.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, f, vp]
         L.swa_prefill_dilated.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, f, vp]
+        L.swa_rope.argtypes = [i, vp, vp, vp, i, i, i, i, f, vp]
+        L.swa_prefill_rope_workspace_size.argtypes = [i, i, i, i, i]
+        L.swa_prefill_rope_workspace_size.restype = sz
+        L.swa_prefill_rope.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp, sz, vp]
         L.swa_longformer_workspace_size.argtypes = [i, i, i, i, i]
         L.swa_longformer_workspace_size.restype = sz
         L.swa_longformer.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, i, f, vp, sz, vp]
@@ -56,7 +60,8 @@ def lib():
         L.swa_debug_index_mask.argtypes = [i, i, i, i, vp, i, vp, vp]
         L.swa_status_str.argtypes = [i]
         L.swa_status_str.restype = ctypes.c_char_p
-        for name in ("swa_prefill", "swa_prefill_sinks", "swa_prefill_dilated",
+        for name in ("swa_prefill", "swa_prefill_sinks", "swa_prefill_dilated", "swa_rope",
+                     "swa_prefill_rope",
                      "swa_prefill_cached", "swa_decode",
                      "swa_cache_write", "swa_cache_append", "swa_longformer",
                      "swa_longformer_proj", "swa_tile_config", "swa_debug_index_mask"):
@@ -148,6 +153,42 @@ def prefill_dilated(q, k, v, W, dilation=None, scale=None, out=None, return_lse=
     _check(lib().swa_prefill_dilated(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T,
                                      Hq, Hkv, D, int(W), dil, sc, _stream(q)),
            "swa_prefill_dilated")
+    return (o, lse) if return_lse else o
+
+
+def rope(x, base, pos=None, out=None):
+    """Rotary positions (rotate-half pairs) of x [B,T,H,D] at positions pos
+    (device int32 [B,T]) or t; out may be x (in place)."""
+    _need(x, "x", 4)
+    if pos is not None:
+        _need(pos, "pos", 2)
+    B, T, H, D = x.shape
+    y = torch.empty_like(x) if out is None else out
+    _check(lib().swa_rope(_dt(x), _ptr(x), _ptr(y), _ptr(pos), B, T, H, D, float(base),
+                          _stream(x)), "swa_rope")
+    return y
+
+
+def prefill_rope_workspace_size(dtype_code, B, T, Hkv, D):
+    return int(lib().swa_prefill_rope_workspace_size(dtype_code, B, T, Hkv, D))
+
+
+def prefill_rope(q, k, v, W, rope_base, scale=None, out=None, workspace=None, return_lse=False):
+    """swa_prefill of rope(q), rope(k), v: q rotated inside the kernel, k rotated
+    once into the workspace."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(B, Hq, T, device=q.device, dtype=torch.float32) if return_lse else None
+    need = prefill_rope_workspace_size(_dt(q), B, T, Hkv, D)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                            device=q.device)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().swa_prefill_rope(_dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq,
+                                  Hkv, D, int(W), float(rope_base), sc, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(q)), "swa_prefill_rope")
     return (o, lse) if return_lse else o
 
 

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libswa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["swa_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "split_kv.hip"]
+SOURCES = ["swa_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "split_kv.hip", "rope.hip"]
 
 # The bf16 kernels never create NaNs (masked scores are -inf, never NaN), so
 # they are built without IEEE NaN quieting: fmax then needs no canonicalising

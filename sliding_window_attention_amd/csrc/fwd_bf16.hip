@@ -331,6 +331,30 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       if (r < n_cls) u = *reinterpret_cast<const U4 *>(qp + ks * 16 + lh * 8);
       qf[ks] = as_bf16x8(u);
     }
+    if constexpr (!SYM && !RING) {
+      if (a.rope) {
+        // Rotary positions, rotate-half pairs (c, c + D/2): this lane holds
+        // columns c = 16ks + 8lh + e, whose partners sit in qf[ks + KS_QK/2].
+        // The angle of pair c is p * base^(-2c/D) (revolutions in float64).
+        const double p = (double)rho + (double)dil * (double)r;
+        const double s1 = a.rope_step, s16 = rope_pow(s1, 16);
+        double rk = a.rope_rev0 * rope_pow(s1, 8 * lh);
+#pragma unroll
+        for (int ks = 0; ks < KS_QK / 2; ++ks) {
+          double ri = rk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float f = rope_frac(p, ri);
+            const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+            const float x = (float)qf[ks][e], y = (float)qf[ks + KS_QK / 2][e];
+            qf[ks][e] = (__bf16)(x * cs - y * sn);
+            qf[ks + KS_QK / 2][e] = (__bf16)(y * cs + x * sn);
+            ri *= s1;
+          }
+          rk *= s16;
+        }
+      }
+    }
     // Make the compiler wait for the Q loads here, before the tile loop: the
     // copies issued in the loop are invisible to its counter tracking, so a
     // wait for Q placed inside the loop would also stall on them.

@@ -60,8 +60,27 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const FwdArgs a, const Glo
     k = kgl;
     v = vgl;
   }
-  for (int d = lane; d < D; d += 64)
-    qs[wave][d] = live ? q[(long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D + d] : 0.f;
+  const float *qrow = q + (long long)b * a.q_sb + (long long)t * a.q_st + (long long)h * D;
+  if (!SYM && !RING && a.rope) {
+    // rotary positions on the query (rotate-half pairs (i, i + D/2) at position t)
+    for (int i = lane; i < D / 2; i += 64) {
+      float xa = 0.f, xb = 0.f;
+      if (live) {
+        xa = qrow[i];
+        xb = qrow[i + D / 2];
+        const double xr = (double)t * (a.rope_rev0 * rope_pow(a.rope_step, i));
+        float sn, cs;
+        sincosf((float)((xr - floor(xr)) * 6.283185307179586), &sn, &cs);
+        const float ra = xa * cs - xb * sn, rb = xb * cs + xa * sn;
+        xa = ra;
+        xb = rb;
+      }
+      qs[wave][i] = xa;
+      qs[wave][i + D / 2] = xb;
+    }
+  } else {
+    for (int d = lane; d < D; d += 64) qs[wave][d] = live ? qrow[d] : 0.f;
+  }
   __syncthreads();
   if (!live) return;
 

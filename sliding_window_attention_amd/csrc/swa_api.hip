@@ -25,6 +25,7 @@ bool dt_ok(swa_dtype dt) { return dt == SWA_BF16 || dt == SWA_F32; }
 bool d_ok(int d) { return d == 64 || d == 128; }
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kRev0 = 0.15915494309189535;  // 1 / 2pi: radians -> revolutions
 
 // Number of splits for split-KV over n_keys keys per (batch, head): enough
 // workgroups to fill the chip (target), each chunk whole 32-key blocks
@@ -231,6 +232,74 @@ swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const
   if (tiles * B > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31)) return SWA_ERR_UNSUPPORTED;
   a.tiles_per_batch = (int)tiles;
   return hip_status(launch_fwd_bf16(a, kCausalDil, d_h, &gl, st));
+}
+
+size_t swa_prefill_rope_workspace_size(swa_dtype dt, int B, int T, int H_kv, int d_h) {
+  if (!dt_ok(dt) || B < 1 || T < 1 || H_kv < 1 || !d_ok(d_h)) return 0;
+  return (size_t)B * T * H_kv * d_h * (dt == SWA_F32 ? 4 : 2);
+}
+
+swa_status swa_rope(swa_dtype dt, const void *x, void *y, const int32_t *pos, int B, int T, int H,
+                    int d_h, float rope_base, void *stream) {
+  if (!dt_ok(dt) || !x || !y || !aligned(x, 16) || !aligned(y, 16) || (pos && !aligned(pos, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || T < 1 || H < 1 || !std::isfinite(rope_base) || !(rope_base > 0.f))
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  return hip_status(launch_rope(dt == SWA_F32, x, y, pos, B, T, H, d_h, kRev0,
+                                std::pow((double)rope_base, -2.0 / d_h),
+                                static_cast<hipStream_t>(stream)));
+}
+
+swa_status swa_prefill_rope(swa_dtype dt, const void *q, const void *k, const void *v, void *o,
+                            float *lse, int B, int T, int H_q, int H_kv, int d_h, int W,
+                            float rope_base, float scale, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (!dt_ok(dt) || !q || !k || !v || !o) return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || T < 1 || H_q < 1 || H_kv < 1 || W < 1 || H_q % H_kv || !scale_ok(scale) ||
+      !std::isfinite(rope_base) || !(rope_base > 0.f))
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  const size_t need = swa_prefill_rope_workspace_size(dt, B, T, H_kv, d_h);
+  if (!workspace || workspace_bytes < need) return SWA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SWA_ERR_INVALID;
+
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = workspace; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.T = T; a.Hq = H_q; a.Hkv = H_kv;
+  a.q_st = (long long)H_q * d_h;
+  a.q_sb = a.q_st * T;
+  a.k_st = (long long)H_kv * d_h;
+  a.k_sb = a.k_st * T;
+  a.k_sh = d_h;
+  a.W = W;
+  a.sl2 = scale * kLog2e;
+  a.group = H_q / H_kv;
+  a.P = prefill_pack(H_q, H_kv);
+  a.NW = fwd_waves(false);
+  a.BM = kRowsPerWave * a.NW / a.P;
+  a.n_qt = (T + a.BM - 1) / a.BM;
+  a.n_hg = H_q / a.P;
+  a.rope = 1;
+  a.rope_rev0 = kRev0;
+  a.rope_step = std::pow((double)rope_base, -2.0 / d_h);
+  GlobalList gl;
+  std::memset(&gl, 0, sizeof(gl));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == SWA_BF16 &&
+      ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31)))
+    return SWA_ERR_UNSUPPORTED;
+  // keys: one rotation pass into the workspace; queries: rotated in registers
+  // by the prefill kernel
+  hipError_t e = launch_rope(dt == SWA_F32, k, workspace, nullptr, B, T, H_kv, d_h, a.rope_rev0,
+                             a.rope_step, st);
+  if (e != hipSuccess) return SWA_ERR_HIP;
+  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, kCausal, d_h, &gl, st));
+  return hip_status(launch_fwd_bf16(a, kCausal, d_h, &gl, st));
 }
 
 swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,

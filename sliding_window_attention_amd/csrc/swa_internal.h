@@ -137,6 +137,23 @@ inline int prefill_pack(int H_q, int H_kv) {
   return (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
 }
 
+// ---------------------------------------------------------------- rotary positions
+//
+// Revolutions of the RoPE angle for pair i at position p: p * rev0 * step^i with
+// rev0 = 1 / 2pi and step = base^(-2/D), in float64 (fp32 would lose ~1e-3 rad
+// at positions ~1e4); step^i by binary powering.  Returned as the fraction in
+// [0, 1), the argument the sine/cosine units take.
+__host__ __device__ inline double rope_pow(double step, int i) {
+  double r = 1.0, s = step;
+  for (; i > 0; i >>= 1, s *= s)
+    if (i & 1) r *= s;
+  return r;
+}
+__host__ __device__ inline float rope_frac(double p, double rev_i) {
+  const double x = p * rev_i;
+  return (float)(x - floor(x));
+}
+
 // ---------------------------------------------------------------- kernel arguments
 
 constexpr int kMaxHeadsLF = 256;
@@ -172,6 +189,11 @@ struct FwdArgs {
   const float *sink_logit;   // [H_q] per-head sink score in the denominator, or null
   // symmetric mode: separate global projections (null = shared with q, k, v)
   const void *qg, *kg, *vg;
+  // rotary positions applied to q in registers (causal modes): the pair
+  // (x_i, x_{i+D/2}) of a row at position p turns by p * rope_rev0 * rope_step^i
+  // revolutions (rope_rev0 = 1 / 2pi, rope_step = base^(-2/D))
+  int rope;
+  double rope_rev0, rope_step;
 };
 
 constexpr int kMaxSinks = 32;  // sink tokens fit the first key tile
@@ -223,6 +245,8 @@ int mfma_qg(int nq);  // queries per pass of the bf16 split kernel
 hipError_t launch_cache_write(bool f32, const void *kn, const void *vn, const int *pos, void *kc,
                               void *vc, int *slot_pos, int B, int L, int S, int Hkv, int D,
                               int n_sink, hipStream_t st);
+hipError_t launch_rope(bool f32, const void *x, void *y, const int *pos, int B, int T, int H, int D,
+                       double rev0, double step, hipStream_t st);
 hipError_t launch_debug_mask(int mode, int T, int w_or_r, int dil, const GlobalList *gl, int G,
                              uint8_t *mask, hipStream_t st);
 

@@ -131,6 +131,31 @@ def test_prefill_dilated_validation():
     assert call([1, 2] * 150, Hq=300, Hkv=1) == UNSUPPORTED  # 300 single-head groups
 
 
+def test_rope_validation():
+    L = bd.lib()
+    assert L.swa_rope(0, None, P, None, 1, 8, 2, 64, 1e4, S0) == INVALID
+    assert L.swa_rope(0, P, P, ctypes.c_void_p(4098), 1, 8, 2, 64, 1e4, S0) == INVALID
+    assert L.swa_rope(0, P, P, None, 1, 8, 2, 64, 0.0, S0) == INVALID
+    assert L.swa_rope(0, P, P, None, 1, 8, 2, 64, float("inf"), S0) == INVALID
+    assert L.swa_rope(0, P, P, None, 0, 8, 2, 64, 1e4, S0) == INVALID
+    assert L.swa_rope(0, P, P, None, 1, 8, 2, 80, 1e4, S0) == UNSUPPORTED
+    need = L.swa_prefill_rope_workspace_size(0, 2, 64, 3, 128)
+    assert need == 2 * 64 * 3 * 128 * 2
+    assert L.swa_prefill_rope_workspace_size(1, 2, 64, 3, 128) == 2 * need
+
+    def pr(ws_bytes=need, base=1e4, **kw):
+        a = dict(Hq=6, Hkv=3, W=8, D=128)
+        a.update(kw)
+        return L.swa_prefill_rope(0, P, P, P, P, None, 2, 64, a["Hq"], a["Hkv"], a["D"], a["W"],
+                                  base, 0.1, P, ws_bytes, S0)
+
+    assert pr(base=-1.0) == INVALID
+    assert pr(W=0) == INVALID
+    assert pr(Hq=5) == INVALID
+    assert pr(D=96) == UNSUPPORTED
+    assert pr(ws_bytes=need - 1) == WORKSPACE
+
+
 def test_longformer_proj_validation():
     assert _lfp(qg=None) == INVALID
     assert _lfp(kg=None) == INVALID
