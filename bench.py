@@ -5,7 +5,8 @@ W=4096, H_q=32, H_kv=8, d_h=128, bf16 (band-TFLOP/s: 4*d_h FLOP per attended
 (query head, key) pair, masked tile work excluded).  The other workloads
 (causal prefill B=2 T=32768 W=1024 local-layer shape, ring decode B=64 W=4096,
 Longformer B=8 T=4096 r=256, chunked prefill of 512-token chunks over a ring
-cache, prefill with attention sinks) are reported in "extra".
+cache, prefill with attention sinks, dilated prefill, prefill with RoPE applied
+inside the call) are reported in "extra".
 
 Timing: inputs resident in HBM, W untimed warm-up launches, then K launches
 bracketed by torch.cuda.synchronize() and HIP events recorded on the stream the
@@ -13,7 +14,8 @@ kernels are launched on (torch's current stream, which the binding passes to
 the library).
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only prefill|local|decode|longformer|chunk|sinks] [--profile-copy]
+                       [--only prefill|local|decode|longformer|chunk|sinks|dilated|rope]
+                       [--profile-copy]
 """
 
 import argparse
@@ -132,6 +134,31 @@ def bench_prefill_sinks(c, n_sink, steps, warmup):
     return dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
 
 
+def dilated_pairs(T, W, d):
+    """Attended pairs per head of the dilated causal window: sum_t min(W, t // d + 1)."""
+    t = np.arange(T, dtype=np.int64)
+    return int(np.minimum(W, t // d + 1).sum())
+
+
+def bench_prefill_dilated(c, dil, steps, warmup):
+    q, k, v = (x.cuda() for x in inp.prefill_inputs(c))
+    o = torch.empty_like(q)
+    ms, _ = time_launches(lambda: bd.prefill_dilated(q, k, v, c.W, dil, out=o), steps, warmup)
+    flops = 4.0 * c.D * c.B * sum(dilated_pairs(c.T, c.W, d) for d in dil)
+    return dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
+
+
+def bench_prefill_rope(c, base, steps, warmup):
+    q, k, v = (x.cuda() for x in inp.prefill_inputs(c))
+    o = torch.empty_like(q)
+    ws = torch.empty(bd.prefill_rope_workspace_size(bd.SWA_BF16, c.B, c.T, c.Hkv, c.D),
+                     dtype=torch.uint8, device="cuda")
+    ms, _ = time_launches(lambda: bd.prefill_rope(q, k, v, c.W, base, out=o, workspace=ws),
+                          steps, warmup)
+    flops = 4.0 * c.D * c.Hq * c.B * causal_pairs(c.T, c.W)
+    return dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
+
+
 def bench_decode(c, steps, warmup):
     q, kc, vc, sp, cur = (x.cuda() for x in inp.decode_inputs(c))
     o = torch.empty_like(q)
@@ -206,7 +233,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "longformer", "local", "chunk",
-                                       "sinks"],
+                                       "sinks", "dilated", "rope"],
                     default="all", help="restrict to one workload (the headline always runs "
                     "unless decode/longformer/local is chosen)")
     ap.add_argument("--profile-copy", action="store_true",
@@ -268,6 +295,24 @@ def main():
                      f"B={c2.B} T={c2.T} W={c2.W} Hq={c2.Hq} Hkv={c2.Hkv} d_h={c2.D} bf16",
             value=round(r7["tflops"], 2), unit="TFLOP/s", ms=round(r7["ms"], 4),
             frac_mfma_peak=round(r7["tflops"] / PEAK_BF16_TFLOPS, 4))
+
+    if args.only in ("all", "dilated"):
+        dil = [1] * 16 + [2] * 8 + [4] * 8
+        r8 = bench_prefill_dilated(c2, dil, max(5, args.steps // 2), args.warmup)
+        extra["prefill_dilated"] = dict(
+            workload=f"causal SWA prefill with dilation 1 on heads 0-15, 2 on 16-23, 4 on 24-31, "
+                     f"B={c2.B} T={c2.T} W={c2.W} Hq={c2.Hq} Hkv={c2.Hkv} d_h={c2.D} bf16",
+            value=round(r8["tflops"], 2), unit="TFLOP/s", ms=round(r8["ms"], 4),
+            frac_mfma_peak=round(r8["tflops"] / PEAK_BF16_TFLOPS, 4))
+
+    if args.only in ("all", "rope"):
+        c3 = inp.C3
+        r9 = bench_prefill_rope(c3, 1.0e4, max(5, args.steps // 2), args.warmup)
+        extra["prefill_rope_local_layer"] = dict(
+            workload="causal SWA prefill B=2 T=32768 W=1024 Hq=32 Hkv=16 d_h=128 bf16 with RoPE "
+                     "(base 1e4) applied inside the call: keys rotated once, queries in registers",
+            value=round(r9["tflops"], 2), unit="TFLOP/s", ms=round(r9["ms"], 4),
+            frac_mfma_peak=round(r9["tflops"] / PEAK_BF16_TFLOPS, 4))
 
     if main_r is None:
         print(json.dumps({"partial": args.only, "extra": extra}), flush=True)

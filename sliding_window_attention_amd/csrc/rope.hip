@@ -18,38 +18,78 @@
 namespace swa {
 namespace {
 
-// Block: D/2 pair columns x (256 / (D/2)) rows per step; the pair's revolution
-// rate rev0 * step^i is computed once per thread.  y may alias x (each thread
-// reads both elements of its pair before writing them).
+// Each thread rotates 8 consecutive pairs (i0 .. i0+7, i0 a multiple of 8) of
+// one row per step: one 16-byte (bf16) or two 16-byte (fp32) accesses per
+// half-row, threads of a row side by side, so a wave reads whole rows.  The
+// pair rates rev0 * step^i are formed once per thread.  y may alias x (each
+// thread reads its elements before writing them).
 template <bool F32>
 __global__ __launch_bounds__(256) void rope_kernel(const void *x, void *y, const int *pos, int T,
                                                   int H, int D, long long rows, double rev0,
                                                   double step) {
   const int half = D / 2;
-  const int i = threadIdx.x % half;
-  const int rpb = 256 / half;  // rows per block step
-  const double rev_i = rev0 * rope_pow(step, i);
-  for (long long row = (long long)blockIdx.x * rpb + threadIdx.x / half; row < rows;
+  const int tpr = half / 8;  // threads per row
+  const int i0 = (threadIdx.x % tpr) * 8;
+  const int rpb = 256 / tpr;  // rows per block step
+  double rv[8];
+  rv[0] = rev0 * rope_pow(step, i0);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) rv[e] = rv[e - 1] * step;
+  for (long long row = (long long)blockIdx.x * rpb + threadIdx.x / tpr; row < rows;
        row += (long long)gridDim.x * rpb) {
     const long long bt = row / H;  // (b, t) of this row
-    const int t = (int)(bt % T);
-    const double p = pos ? (double)pos[bt] : (double)t;
-    const double xr = p * rev_i;
-    const float ang = (float)((xr - floor(xr)) * 6.283185307179586);
-    float sn, cs;
-    sincosf(ang, &sn, &cs);
-    const long long o0 = row * D + i, o1 = o0 + half;
+    const double p = pos ? (double)pos[bt] : (double)(int)(bt % T);
+    const long long o0 = row * D + i0, o1 = o0 + half;
+    float a[8], b[8];
     if constexpr (F32) {
-      const float a = static_cast<const float *>(x)[o0], b = static_cast<const float *>(x)[o1];
-      static_cast<float *>(y)[o0] = a * cs - b * sn;
-      static_cast<float *>(y)[o1] = b * cs + a * sn;
+      const float4 *xa = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + o0);
+      const float4 *xb = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + o1);
+      const float4 a0 = xa[0], a1 = xa[1], b0 = xb[0], b1 = xb[1];
+      a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+      a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+      b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+      b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
     } else {
-      const uint16_t ua = static_cast<const uint16_t *>(x)[o0];
-      const uint16_t ub = static_cast<const uint16_t *>(x)[o1];
-      const float a = __uint_as_float((uint32_t)ua << 16), b = __uint_as_float((uint32_t)ub << 16);
-      const __bf16 ra = (__bf16)(a * cs - b * sn), rb = (__bf16)(b * cs + a * sn);
-      static_cast<uint16_t *>(y)[o0] = __builtin_bit_cast(uint16_t, ra);
-      static_cast<uint16_t *>(y)[o1] = __builtin_bit_cast(uint16_t, rb);
+      const uint4 ua = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + o0);
+      const uint4 ub = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + o1);
+      const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a[2 * w] = __uint_as_float(wa[w] << 16);
+        a[2 * w + 1] = __uint_as_float(wa[w] & 0xffff0000u);
+        b[2 * w] = __uint_as_float(wb[w] << 16);
+        b[2 * w + 1] = __uint_as_float(wb[w] & 0xffff0000u);
+      }
+    }
+    float ra[8], rb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double xr = p * rv[e];
+      float sn, cs;
+      sincosf((float)((xr - floor(xr)) * 6.283185307179586), &sn, &cs);
+      ra[e] = a[e] * cs - b[e] * sn;
+      rb[e] = b[e] * cs + a[e] * sn;
+    }
+    if constexpr (F32) {
+      float4 *ya = reinterpret_cast<float4 *>(static_cast<float *>(y) + o0);
+      float4 *yb = reinterpret_cast<float4 *>(static_cast<float *>(y) + o1);
+      ya[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
+      ya[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
+      yb[0] = make_float4(rb[0], rb[1], rb[2], rb[3]);
+      yb[1] = make_float4(rb[4], rb[5], rb[6], rb[7]);
+    } else {
+      uint32_t wa[4], wb[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const __bf16 a0 = (__bf16)ra[2 * w], a1 = (__bf16)ra[2 * w + 1];
+        const __bf16 b0 = (__bf16)rb[2 * w], b1 = (__bf16)rb[2 * w + 1];
+        wa[w] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        wb[w] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      }
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + o0) = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(y) + o1) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
     }
   }
 }
@@ -59,9 +99,9 @@ __global__ __launch_bounds__(256) void rope_kernel(const void *x, void *y, const
 hipError_t launch_rope(bool f32, const void *x, void *y, const int *pos, int B, int T, int H, int D,
                        double rev0, double step, hipStream_t st) {
   const long long rows = (long long)B * T * H;
-  const int rpb = 256 / (D / 2);
+  const int rpb = 256 / (D / 16);  // rows per block step: 8 pairs per thread
   long long blocks = (rows + rpb - 1) / rpb;
-  if (blocks > 65536) blocks = 65536;
+  if (blocks > 8192) blocks = 8192;
   if (blocks <= 0) return hipSuccess;
   if (f32)
     hipLaunchKernelGGL(rope_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, x, y, pos, T, H,
