@@ -19,6 +19,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -306,7 +307,7 @@ def main():
             frac_mfma_peak=round(r8["tflops"] / PEAK_BF16_TFLOPS, 4))
 
     if args.only in ("all", "rope"):
-        c3 = inp.C3
+        c3 = dataclasses.replace(inp.C3, rope=False)  # the call applies the rotation
         r9 = bench_prefill_rope(c3, 1.0e4, max(5, args.steps // 2), args.warmup)
         extra["prefill_rope_local_layer"] = dict(
             workload="causal SWA prefill B=2 T=32768 W=1024 Hq=32 Hkv=16 d_h=128 bf16 with RoPE "
