@@ -165,6 +165,30 @@ __device__ inline void dma_tile(const char *gbase, const uint32_t *off, uint32_t
   }
 }
 
+// A whole K/V tile stage from one wave: two copies from the K rows and two
+// from the V rows (scalar bases kb, vb, per-lane offsets off[0..3]), landing at
+// LDS lds, lds + step, lds + 2 step, lds + 3 step (step = the waves' stride
+// through the stage, 1 KB per wave).  One block, no branches.
+template <int STEP>
+__device__ inline void dma_kv4(const char *kb, const char *vb, const uint32_t *off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %4, %2\n\t"
+      "s_add_u32 m0, m0, %8\n\t"
+      "global_load_lds_dwordx4 %5, %2\n\t"
+      "s_add_u32 m0, m0, %8\n\t"
+      "global_load_lds_dwordx4 %6, %3\n\t"
+      "s_add_u32 m0, m0, %8\n\t"
+      "global_load_lds_dwordx4 %7, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(uni_u32(lds)), "s"(uni_ptr(kb)), "s"(uni_ptr(vb)), "v"(off[0]), "v"(off[1]), "v"(off[2]),
+        "v"(off[3]), "i"(STEP)
+      : "scc");
+}
+
 // One 4-byte copy per lane (global_load_lds_dword): lane i's word lands at LDS
 // byte m0 + 4*i.
 __device__ inline void dma_dword(const char *gbase, uint32_t off, uint32_t lds) {
@@ -221,7 +245,8 @@ struct IntC {
 constexpr float kLazy = 8.f;
 
 // NW waves per workgroup; three waves per SIMD (12 per CU) bound the registers.
-// MODE: kCausal, kSymmetric, kRing, kCausalSink or kSymmetricProj (FwdMode).
+// MODE: kCausal, kSymmetric, kRing, kCausalSink, kSymmetricProj or kCausalDil
+// (FwdMode).
 template <int D, int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
     const FwdArgs a, const GlobalList gl) {
@@ -419,10 +444,17 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
             : 0;
   // DMA of the K and V rows of tile j (window tiles j < n_win, then tiles of
   // global keys) into the stage at LDS address `stage`.
+  // Four copies per wave, the first two K rows and the last two V rows (four
+  // waves): a whole window tile goes out as one branch-free block.
+  constexpr bool KV4 = NSLOT == 4 && NSLOT * NW == 2 * Gm::NI && Gm::NI == 2 * NW;
   auto issue = [&](int j, uint32_t stage) {
     const int kt = (j < n_win) ? tr.lo + j : 0;  // key tile (sink tile: 0)
     const bool whole = (j < n_win || !SYM) && kt * BN + BN <= n_keyrows;
     const long long base = (k_rho + (long long)kt * BN * k_rowstride) * 2;
+    if (KV4 && whole && j < n_win) {
+      const char *kt8 = kb8 + base;
+      dma_kv4<NW * 1024>(kt8, kt8 + d_v, loff, stage + (uint32_t)wave * 1024u);
+    } else {
 #pragma unroll
     for (int t = 0; t < NSLOT; ++t) {
       const int i = wave + t * NW;
@@ -452,6 +484,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           dma_tile<1>(g8, &off, ld);
         }
       }
+    }
     }
     if constexpr (RING) {
       // the tile's slot positions (lane i: slot tile*BN + i, clamped; the
@@ -833,7 +866,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *
   const int nblk = (sym || mode == kCausalDil) ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
   if (nblk <= 0) return hipSuccess;
   constexpr int NWC = SWA_FWD_WAVES;
-  if (a.NW != (sym ? 4 : NWC)) return hipErrorInvalidValue;
+  if (a.NW != fwd_waves(mode)) return hipErrorInvalidValue;
   dim3 grid(nblk), block(64 * a.NW);
   if (mode == kCausal) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausal, NWC>), grid, block, 0, st, a, *gl);

@@ -89,9 +89,9 @@ swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *
   if (!BM || !BN || H_q < 1 || H_kv < 1 || H_q % H_kv) return SWA_ERR_INVALID;
   if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
   if (entry == 'p') {
-    *BM = kRowsPerWave * fwd_waves(false) / prefill_pack(H_q, H_kv);
+    *BM = kRowsPerWave * fwd_waves(kCausal) / prefill_pack(H_q, H_kv);
   } else if (entry == 'l') {
-    *BM = kRowsPerWave * fwd_waves(true);
+    *BM = kRowsPerWave * fwd_waves(kSymmetric);
   } else {
     return SWA_ERR_INVALID;
   }
@@ -157,15 +157,15 @@ swa_status swa_prefill_sinks(swa_dtype dt, const void *q, const void *k, const v
   a.W = W;
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
+  const int mode = (n_sink > 0 || sink_logit) ? kCausalSink : kCausal;
   a.P = prefill_pack(H_q, H_kv);
-  a.NW = fwd_waves(false);
+  a.NW = fwd_waves(mode);
   a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (T + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int mode = (n_sink > 0 || sink_logit) ? kCausalSink : kCausal;
   if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, mode, d_h, &gl, st));
   // bf16 kernels address one batch slice of K/V with 32-bit byte offsets
   if ((long long)B * a.n_hg * a.n_qt > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31))
@@ -217,7 +217,7 @@ swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const
   for (int h = 0; h < H_q && P > 1; ++h)
     if (dilation[h] != dilation[h - h % P]) P = 1;
   a.P = P;
-  a.NW = fwd_waves(false);
+  a.NW = fwd_waves(kCausalDil);
   a.BM = kRowsPerWave * a.NW / P;
   a.n_hg = H_q / P;
   if (a.n_hg > kMaxHeadsLF) return SWA_ERR_UNSUPPORTED;
@@ -280,7 +280,7 @@ swa_status swa_prefill_rope(swa_dtype dt, const void *q, const void *k, const vo
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
   a.P = prefill_pack(H_q, H_kv);
-  a.NW = fwd_waves(false);
+  a.NW = fwd_waves(kCausal);
   a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (T + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
@@ -330,7 +330,7 @@ swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
   a.P = prefill_pack(H_q, H_kv);
-  a.NW = fwd_waves(false);
+  a.NW = fwd_waves(kRing);
   a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (L + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
@@ -494,7 +494,7 @@ swa_status longformer_impl(swa_dtype dt, const void *q, const void *k, const voi
   a.sl2 = scale * kLog2e;
   a.group = 1;
   a.P = 1;
-  a.NW = fwd_waves(true);
+  a.NW = fwd_waves(kSymmetric);
   a.BM = kRowsPerWave * a.NW;
   a.G = G;
   long long tiles = 0;

@@ -126,7 +126,7 @@ constexpr int kRowsPerWave = 32; // query rows per wave (one 32x32 MFMA block)
 #ifndef SWA_FWD_WAVES
 #define SWA_FWD_WAVES 4
 #endif
-inline int fwd_waves(bool symmetric) { return symmetric ? 4 : SWA_FWD_WAVES; }
+
 
 // Heads packed into one workgroup for the causal kernel: waves of one
 // workgroup take query heads that share a key/value head, so a staged K/V tile
@@ -210,6 +210,11 @@ enum FwdMode {
   kSymmetricProj = 4,
   kCausalDil = 5
 };
+
+// Waves per workgroup of the banded kernel for a window family.
+inline int fwd_waves(int mode) {
+  return (mode == kSymmetric || mode == kSymmetricProj) ? 4 : SWA_FWD_WAVES;
+}
 
 struct GlobalList {
   int idx[kMaxGlobalsLF];  // [B][G] positions
