@@ -642,19 +642,26 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     pos_hi = uni(hi);
     asm volatile("" ::"v"(my_pos));
   }
-  // Ring tile with every (valid row, slot) pair attended: all slots exist,
-  // are filled and lie in the window of every row of the wave.
-  auto ring_full = [&](const char *stg, int j) {
+  // Ring tile class for the rows of this wave (query positions in
+  // [pos_lo, pos_hi]): 1 = every (row, slot) pair attended (all slots exist,
+  // are filled and lie in the window of every row), 0 = no slot lies in the
+  // window of any row (nor is a sink), so the tile adds nothing and is
+  // skipped, 2 = partial (masked).
+  auto ring_class = [&](const char *stg, int j) {
     const int n_in = min(BN, a.S - (tr.lo + j) * BN);
     const int sp = reinterpret_cast<const int *>(stg + SP_OFF)[lane % BN];
+    const bool live = (lane % BN) < n_in && sp >= 0 && sp <= pos_hi &&
+                      ((long long)sp > (long long)pos_lo - a.W || sp < a.n_sink);
+    if (__builtin_amdgcn_ballot_w64(live) == 0) return 0;
     int lo = sp, hi = sp;
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) {
       lo = min(lo, __shfl_xor(lo, x));
       hi = max(hi, __shfl_xor(hi, x));
     }
-    return n_in == BN && uni(lo) >= 0 && (long long)uni(lo) > (long long)pos_hi - a.W &&
-           uni(hi) <= pos_lo;
+    const bool full = n_in == BN && uni(lo) >= 0 &&
+                      (long long)uni(lo) > (long long)pos_hi - a.W && uni(hi) <= pos_lo;
+    return full ? 1 : 2;
   };
   // Ring mask: slot k of the tile (k < S) is attended iff its position p has
   // p >= 0 and my_pos - W < p <= my_pos.
@@ -774,13 +781,16 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     const int kj = tr.lo + j;
     // a wave computes the tiles of its rows' band, the extra tiles, and key
     // tile 0 when sink tokens live there
-    if (has_rows && (j >= n_win || (kj >= wr.lo && kj <= wr.hi) || (CSINK && a.n_sink > 0 && kj == 0))) {
-      const char *ks = smem + st * STAGE_B;
+    const char *ks = smem + st * STAGE_B;
+    int rc = 1;  // ring mode: tile class (0 = nothing attended, skip)
+    if constexpr (RING) rc = has_rows ? ring_class(ks, j) : 0;
+    if (has_rows && rc != 0 &&
+        (j >= n_win || (kj >= wr.lo && kj <= wr.hi) || (CSINK && a.n_sink > 0 && kj == 0))) {
       f32x16 sv[KB];
       U4 pu[PK];
       qk(ks, sv);
       if constexpr (RING) {
-        if (!ring_full(ks, j)) ring_mask(ks, j, sv);
+        if (rc == 2) ring_mask(ks, j, sv);
       } else {
         const uint64_t gcols = glob_cols(j);
         if (gcols || !tile_full(j)) mask(j, sv, gcols);

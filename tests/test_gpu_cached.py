@@ -47,6 +47,7 @@ def _compare(q, kc, vc, sp, qp, W, dtype, rows=None):
     (2, 130, 629, 500, 16, 8, 64, 500, 2000),
     (2, 48, 64, 40, 4, 2, 128, 0, 10),        # ring not yet full (empty slots)
     (2, 40, 50, 40, 4, 2, 128, 100, 200),     # ring smaller than W+L-1: early queries lost keys
+    (2, 64, 600, 40, 8, 2, 128, 1000, 1100),  # most slot tiles outside every window (skipped)
 ])
 def test_cached_matches_oracle(dtype, B, L, S, W, Hq, Hkv, D, p_lo, p_hi):
     c = inp.ChunkCase(B=B, L=L, S=S, W=W, Hq=Hq, Hkv=Hkv, D=D, p_lo=p_lo, p_hi=p_hi, dtype=dtype,
