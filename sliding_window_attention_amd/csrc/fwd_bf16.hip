@@ -24,7 +24,7 @@
 // The score definition is the masked softmax of [KB] §2 (alpha^SWA, o^SWA);
 // windows: causal t-W < s <= t ([KB] §2-§3); in symmetric mode, the
 // undilated window |i-j| <= r inside one residue class of a dilated head plus
-// the global keys not already in the window ([PP] §1.1, §3.1, §4.3); in ring
+// the global keys, each key once ([PP] §1.1, §3.1, §4.3); in ring
 // mode, a chunk of queries with absolute positions against the slots of a ring
 // cache, slot attended iff its stored position p has q_pos-W < p <= q_pos
 // ([G3] "How it works": the window comes from positions, not buffer offsets).
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   const int n_win = tr.hi - tr.lo + 1;
   // extra tiles after the window: global keys (symmetric), or key tile 0 for
   // the sink tokens when the window tiles do not reach it (causal)
-  const int n_glob = SYM ? ceil_div(a.G, BN) : (CSINK && a.n_sink > 0 && tr.lo > 0) ? 1 : 0;
+  const int n_glob = GPROJ ? ceil_div(a.G, BN) : (CSINK && a.n_sink > 0 && tr.lo > 0) ? 1 : 0;
   const int n_tiles = n_win + n_glob;
   // this wave's valid rows [row0, w_last] and the window tiles they need
   const int w_last = min(row0 + kRowsPerWave, n_cls) - 1;
@@ -602,12 +602,16 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       }
     }
   };
-  // Separate global projections: columns of window tile j holding a global
-  // position of this residue class (uniform; the loop runs over the globals).
+  // With separate global projections (or many globals): columns of window
+  // tile j holding a global position of this residue class (uniform; the loop
+  // runs over the globals).  The window tiles mask them and the tile of global
+  // keys attends every global, so a global inside a row's window is counted
+  // once (and, with separate projections, read through K_g).  Plain symmetric
+  // mode adds its few global keys after the band instead (see below).
   auto glob_cols = [&](int j) -> uint64_t {
     uint64_t m = 0;
     if constexpr (GPROJ) {
-      if (j < n_win) {
+      if (j < n_win && a.G > 0) {
         const int c0 = (tr.lo + j) * BN;
         for (int u = 0; u < a.G; ++u) {
           const int d = gl.idx[b * a.G + u] - rho;
@@ -689,8 +693,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   // the class length.
   const int lo_key = SYM ? my_row - a.W : my_row - a.W + 1;
   const int hi_key = min(SYM ? my_row + a.W : my_row, n_cls - 1);
-  // mask of a partial tile: window predicate, or for a tile of global keys
-  // the globals not already inside this row's (dilated) window
+  // mask of a partial tile: the window predicate (global positions left out
+  // when gcols marks some), or for a tile of global keys the existing globals
   auto mask = [&](int j, f32x16 *sv, uint64_t gcols) {
     if (j < n_win) {
       // key of element (kb, e) = tile base + 4*lh + c(kb, e); compare c with
@@ -698,7 +702,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       const int base = (tr.lo + j) * BN + 4 * lh;
       const int lo = lo_key - base, hi = hi_key - base;
       if (GPROJ && gcols) {
-        // global positions of this class in the tile go through K_g instead
+        // global positions of this class in the tile: counted in the global tile
         const uint64_t gl_lane = gcols >> (4 * lh);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -743,25 +747,16 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
         }
       return;
     }
-    // Tile of global keys: column c holds global u0 + c.  Bit c of okb is set
-    // when that global exists and is not already inside row my_row's
-    // (dilated) window, where the window tiles count it.  The loop runs over
-    // the tile's globals only (often just a few).
-    const int u0 = (j - n_win) * BN;
-    const int ng = min(a.G - u0, BN);
-    const int i_abs = rho + dil * my_row;
-    uint64_t okb = 0;
-    for (int c = 0; c < ng; ++c) {
-      const int g = gl.idx[b * a.G + u0 + c];
-      if (GPROJ || !dilated_in(i_abs, g, a.W, dil)) okb |= 1ull << c;
-    }
-    okb >>= 4 * lh;  // this lane's columns are 4*lh + c(kb, e)
+    // Tile of global keys: column c holds global u0 + c.  Every existing global
+    // is attended here; the window tiles leave global positions out
+    // (glob_cols), so each key is counted once.
+    const int hi = min(a.G - (j - n_win) * BN, BN) - 1 - 4 * lh;  // this lane's origin
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
-        if (!((okb >> c) & 1)) sv[kb][e] = -INFINITY;
+        if (c > hi) sv[kb][e] = -INFINITY;
       }
   };
 
@@ -811,6 +806,50 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       if (j + 2 < n_tiles) step(j + 2, IntC<2 % NST>{});
     if constexpr (NST > 3)
       if (j + 3 < n_tiles) step(j + 3, IntC<3 % NST>{});
+  }
+  if constexpr (MODE == kSymmetric) {
+    // The global keys (few: at most kValuGlobals), one at a time in registers:
+    // each lane holds half of its row's q and forms the other half's partial
+    // dot product through the partner lane; a global already inside the row's
+    // (dilated) window was counted by the band and is skipped.  The state
+    // (m, l, O) is updated as for a tile of one key; P stays in fp32.
+    if (a.G > 0 && has_rows) {
+      const int i_abs = rho + dil * my_row;
+      const char *kb_row = reinterpret_cast<const char *>(kg) + ((long long)b * a.k_sb + (long long)kvh * a.k_sh) * 2;
+      const char *vb_row = reinterpret_cast<const char *>(vg) + ((long long)b * a.k_sb + (long long)kvh * a.k_sh) * 2;
+      for (int u = 0; u < a.G; ++u) {
+        const int g = gl.idx[b * a.G + u];
+        const char *kr = kb_row + (long long)g * a.k_st * 2;
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS_QK; ++ks) {
+          const U4 kk = *reinterpret_cast<const U4 *>(kr + (ks * 16 + lh * 8) * 2);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            part = fmaf((float)qf[ks][2 * w], __uint_as_float(kk.w[w] << 16), part);
+            part = fmaf((float)qf[ks][2 * w + 1], __uint_as_float(kk.w[w] & 0xffff0000u), part);
+          }
+        }
+        const float dot = xhalf_add(part);
+        const bool take = my_row < n_cls && !dilated_in(i_abs, g, a.W, dil);
+        const float sg = take ? dot * a.sl2 : -INFINITY;
+        rescale(sg);
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const float pg = take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f;
+        l_run += pg;
+        const char *vr = vb_row + (long long)g * a.k_st * 2;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const uint2 vv = *reinterpret_cast<const uint2 *>(vr + (db * 32 + 8 * g4 + 4 * lh) * 2);
+            acc_o[db][4 * g4 + 0] = fmaf(pg, __uint_as_float(vv.x << 16), acc_o[db][4 * g4 + 0]);
+            acc_o[db][4 * g4 + 1] = fmaf(pg, __uint_as_float(vv.x & 0xffff0000u), acc_o[db][4 * g4 + 1]);
+            acc_o[db][4 * g4 + 2] = fmaf(pg, __uint_as_float(vv.y << 16), acc_o[db][4 * g4 + 2]);
+            acc_o[db][4 * g4 + 3] = fmaf(pg, __uint_as_float(vv.y & 0xffff0000u), acc_o[db][4 * g4 + 3]);
+          }
+      }
+    }
   }
   // other waves may still read the last stage, which the output staging reuses
   __syncthreads();

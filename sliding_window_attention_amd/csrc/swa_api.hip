@@ -513,14 +513,20 @@ swa_status longformer_impl(swa_dtype dt, const void *q, const void *k, const voi
   if (gproj) {
     a.qg = qg; a.kg = kg; a.vg = vg;
   }
+  // Many global tokens: the tile-of-global-keys kernel, which with shared
+  // projections reads the global keys from k, v themselves.
+  const bool gtile = gproj || G > kValuGlobals;
+  if (gtile && !gproj) {
+    a.qg = q; a.kg = k; a.vg = v;
+  }
   GlobalList gl;
   std::memset(&gl, 0, sizeof(gl));
   for (int i = 0; i < B * G; ++i) gl.idx[i] = global_idx[i];
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int mode = gproj ? kSymmetricProj : kSymmetric;
-  if (dt == SWA_F32) return hip_status(launch_fwd_f32(a, mode, d_h, &gl, st));
+  if (dt == SWA_F32)
+    return hip_status(launch_fwd_f32(a, gproj ? kSymmetricProj : kSymmetric, d_h, &gl, st));
 
-  hipError_t e = launch_fwd_bf16(a, mode, d_h, &gl, st);
+  hipError_t e = launch_fwd_bf16(a, gtile ? kSymmetricProj : kSymmetric, d_h, &gl, st);
   if (e != hipSuccess || G == 0) return hip_status(e);
   // Global rows attend every position: split-KV over all T keys, written after
   // (stream order) the local pass, replacing those rows.  With separate

@@ -197,6 +197,9 @@ struct FwdArgs {
 };
 
 constexpr int kMaxSinks = 32;  // sink tokens fit the first key tile
+// Longformer mode: up to this many global tokens per row the banded kernel adds
+// the global keys after the band in registers; more take a tile of global keys.
+constexpr int kValuGlobals = 32;
 
 // Window families of the banded kernels (kCausalSink: causal plus attention
 // sinks, a separate instantiation so the plain causal kernel carries none of it).

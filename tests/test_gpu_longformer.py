@@ -26,6 +26,9 @@ SMALL = [
     (2, 520, 4, 64, 64, [1, 1, 2, 2], [[0, 8], [200, 519]]),
     (1, 129, 2, 128, 63, [4, 1], [[3, 64, 65, 100]]),
     (1, 90, 2, 64, 5, [100, 1], [[0]]),
+    # more than 32 global tokens: the tile-of-global-keys path with shared projections
+    (1, 300, 2, 64, 9, [1, 3], [list(range(0, 300, 7))]),
+    (2, 260, 2, 128, 20, [2, 1], [list(range(3, 260, 6)), list(range(0, 43))]),
 ]
 
 
