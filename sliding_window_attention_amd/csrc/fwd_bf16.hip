@@ -33,7 +33,9 @@
 // does for dilated Longformer heads.
 // Causal and ring modes take attention sinks: the first n_sink positions stay
 // visible next to the window ([KB] §4 "Failure mode 1"; [ST] "What's New"), and
-// an optional per-head sink score joins the softmax denominator.  Symmetric
+// an optional per-head sink score joins the softmax denominator.  In causal
+// mode the band counts the sinks inside a row's window; those before it are
+// added after the band, one key at a time in registers.  Symmetric
 // mode may take separate global projections ([PP] §5.2): every global key of a
 // local row then comes from K_g, V_g (the window tiles drop global positions).
 //
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   const int n_win = tr.hi - tr.lo + 1;
   // extra tiles after the window: global keys (symmetric), or key tile 0 for
   // the sink tokens when the window tiles do not reach it (causal)
-  const int n_glob = GPROJ ? ceil_div(a.G, BN) : (CSINK && a.n_sink > 0 && tr.lo > 0) ? 1 : 0;
+  const int n_glob = GPROJ ? ceil_div(a.G, BN) : 0;
   const int n_tiles = n_win + n_glob;
   // this wave's valid rows [row0, w_last] and the window tiles they need
   const int w_last = min(row0 + kRowsPerWave, n_cls) - 1;
@@ -713,18 +715,6 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           }
         return;
       }
-      if (CSINK && a.n_sink > 0 && tr.lo + j == 0) {
-        // key tile 0 inside the window range: sinks s < n_sink, s <= t join
-        const int hs = min(a.n_sink - 1, my_row) - base;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
-            if ((c < lo || c > hi) && c > hs) sv[kb][e] = -INFINITY;
-          }
-        return;
-      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -734,19 +724,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
         }
       return;
     }
-    if constexpr (!SYM) {
-      if constexpr (!CSINK) return;
-      // the sink tile (key tile 0, outside every row's window): s < n_sink
-      const int hs = a.n_sink - 1 - 4 * lh;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
-          if (c > hs) sv[kb][e] = -INFINITY;
-        }
-      return;
-    }
+    if constexpr (!SYM) return;
     // Tile of global keys: column c holds global u0 + c.  Every existing global
     // is attended here; the window tiles leave global positions out
     // (glob_cols), so each key is counted once.
@@ -780,7 +758,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     int rc = 1;  // ring mode: tile class (0 = nothing attended, skip)
     if constexpr (RING) rc = has_rows ? ring_class(ks, j) : 0;
     if (has_rows && rc != 0 &&
-        (j >= n_win || (kj >= wr.lo && kj <= wr.hi) || (CSINK && a.n_sink > 0 && kj == 0))) {
+        (j >= n_win || (kj >= wr.lo && kj <= wr.hi))) {
       f32x16 sv[KB];
       U4 pu[PK];
       qk(ks, sv);
@@ -807,49 +785,58 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     if constexpr (NST > 3)
       if (j + 3 < n_tiles) step(j + 3, IntC<3 % NST>{});
   }
-  if constexpr (MODE == kSymmetric) {
-    // The global keys (few: at most kValuGlobals), one at a time in registers:
-    // each lane holds half of its row's q and forms the other half's partial
-    // dot product through the partner lane; a global already inside the row's
-    // (dilated) window was counted by the band and is skipped.  The state
-    // (m, l, O) is updated as for a tile of one key; P stays in fp32.
-    if (a.G > 0 && has_rows) {
-      const int i_abs = rho + dil * my_row;
-      const char *kb_row = reinterpret_cast<const char *>(kg) + ((long long)b * a.k_sb + (long long)kvh * a.k_sh) * 2;
-      const char *vb_row = reinterpret_cast<const char *>(vg) + ((long long)b * a.k_sb + (long long)kvh * a.k_sh) * 2;
-      for (int u = 0; u < a.G; ++u) {
-        const int g = gl.idx[b * a.G + u];
-        const char *kr = kb_row + (long long)g * a.k_st * 2;
-        float part = 0.f;
+  // Keys outside the band, one at a time in registers: the few global keys of
+  // Longformer mode (at most kValuGlobals) and the sink tokens of causal mode.
+  // Each lane holds half of its row's q and forms the other half's partial dot
+  // product through the partner lane; the state (m, l, O) is updated as for a
+  // tile of one key, with P in fp32.  `take` drops keys the band already
+  // counted (and rows past the end).
+  auto extra_key = [&](int key_pos, bool take) {
+    const long long kv_row = ((long long)b * a.k_sb + (long long)kvh * a.k_sh + (long long)key_pos * a.k_st) * 2;
+    const char *kr = reinterpret_cast<const char *>(kg) + kv_row;
+    float part = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS_QK; ++ks) {
-          const U4 kk = *reinterpret_cast<const U4 *>(kr + (ks * 16 + lh * 8) * 2);
+    for (int ks = 0; ks < KS_QK; ++ks) {
+      const U4 kk = *reinterpret_cast<const U4 *>(kr + (ks * 16 + lh * 8) * 2);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            part = fmaf((float)qf[ks][2 * w], __uint_as_float(kk.w[w] << 16), part);
-            part = fmaf((float)qf[ks][2 * w + 1], __uint_as_float(kk.w[w] & 0xffff0000u), part);
-          }
-        }
-        const float dot = xhalf_add(part);
-        const bool take = my_row < n_cls && !dilated_in(i_abs, g, a.W, dil);
-        const float sg = take ? dot * a.sl2 : -INFINITY;
-        rescale(sg);
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        const float pg = take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f;
-        l_run += pg;
-        const char *vr = vb_row + (long long)g * a.k_st * 2;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const uint2 vv = *reinterpret_cast<const uint2 *>(vr + (db * 32 + 8 * g4 + 4 * lh) * 2);
-            acc_o[db][4 * g4 + 0] = fmaf(pg, __uint_as_float(vv.x << 16), acc_o[db][4 * g4 + 0]);
-            acc_o[db][4 * g4 + 1] = fmaf(pg, __uint_as_float(vv.x & 0xffff0000u), acc_o[db][4 * g4 + 1]);
-            acc_o[db][4 * g4 + 2] = fmaf(pg, __uint_as_float(vv.y << 16), acc_o[db][4 * g4 + 2]);
-            acc_o[db][4 * g4 + 3] = fmaf(pg, __uint_as_float(vv.y & 0xffff0000u), acc_o[db][4 * g4 + 3]);
-          }
+      for (int w = 0; w < 4; ++w) {
+        part = fmaf((float)qf[ks][2 * w], __uint_as_float(kk.w[w] << 16), part);
+        part = fmaf((float)qf[ks][2 * w + 1], __uint_as_float(kk.w[w] & 0xffff0000u), part);
       }
     }
+    const float dot = xhalf_add(part);
+    const float sg = take ? dot * a.sl2 : -INFINITY;
+    rescale(sg);
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    const float pg = take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f;
+    l_run += pg;
+    const char *vr = reinterpret_cast<const char *>(vg) + kv_row;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint2 vv = *reinterpret_cast<const uint2 *>(vr + (db * 32 + 8 * g4 + 4 * lh) * 2);
+        acc_o[db][4 * g4 + 0] = fmaf(pg, __uint_as_float(vv.x << 16), acc_o[db][4 * g4 + 0]);
+        acc_o[db][4 * g4 + 1] = fmaf(pg, __uint_as_float(vv.x & 0xffff0000u), acc_o[db][4 * g4 + 1]);
+        acc_o[db][4 * g4 + 2] = fmaf(pg, __uint_as_float(vv.y << 16), acc_o[db][4 * g4 + 2]);
+        acc_o[db][4 * g4 + 3] = fmaf(pg, __uint_as_float(vv.y & 0xffff0000u), acc_o[db][4 * g4 + 3]);
+      }
+  };
+  if constexpr (MODE == kSymmetric) {
+    // global keys; one already inside the row's (dilated) window is skipped
+    if (a.G > 0 && has_rows) {
+      const int i_abs = rho + dil * my_row;
+      for (int u = 0; u < a.G; ++u) {
+        const int g = gl.idx[b * a.G + u];
+        extra_key(g, my_row < n_cls && !dilated_in(i_abs, g, a.W, dil));
+      }
+    }
+  }
+  if constexpr (CSINK) {
+    // sink tokens s < n_sink before the row's window (s <= t - W); those
+    // inside it were counted by the band
+    if (has_rows)
+      for (int sk = 0; sk < a.n_sink; ++sk) extra_key(sk, my_row < n_cls && sk <= my_row - a.W);
   }
   // other waves may still read the last stage, which the output staging reuses
   __syncthreads();

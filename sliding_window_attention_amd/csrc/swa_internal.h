@@ -196,7 +196,7 @@ struct FwdArgs {
   double rope_rev0, rope_step;
 };
 
-constexpr int kMaxSinks = 32;  // sink tokens fit the first key tile
+constexpr int kMaxSinks = 32;  // few: the causal kernel adds them one key at a time
 // Longformer mode: up to this many global tokens per row the banded kernel adds
 // the global keys after the band in registers; more take a tile of global keys.
 constexpr int kValuGlobals = 32;
