@@ -220,7 +220,14 @@ swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
  *   global_idx : HOST int32 [B, G]; each row strictly increasing in [0, T);
  *                NULL iff G == 0; B*G <= 512
  *   workspace  : device scratch of at least swa_longformer_workspace_size()
- *                bytes (0 when G == 0), 256-byte aligned, caller-owned.
+ *                bytes (0 when G == 0), 256-byte aligned, caller-owned.  With
+ *                bf16 the global rows then come from partial states the banded
+ *                pass leaves per 32-key block (B*H*G*n_blk records of d_h+4
+ *                floats, n_blk = the most 32-key class blocks of any head; the
+ *                reported size covers every head dilation up to 16); a head
+ *                with a larger dilation, or a workspace too small for those
+ *                records, takes a separate split-KV pass over K and V instead
+ *                (same results within rounding).
  * Errors: INVALID for r < 0, bad dilation or global list, and the swa_prefill
  * cases; UNSUPPORTED for other d_h, H > 256 or B*G > 512; WORKSPACE. */
 size_t swa_longformer_workspace_size(int B, int T, int H, int d_h, int G);

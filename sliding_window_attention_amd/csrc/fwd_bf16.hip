@@ -55,6 +55,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct alignas(16) U4 {
   uint32_t w[4];
@@ -105,6 +106,10 @@ __device__ inline int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1
 template <int D>
 __device__ inline int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
+
+// Workgroup barrier for LDS reuse: waits for this wave's LDS operations but,
+// unlike __syncthreads and its fences, not for its global loads and stores.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ inline uint32_t lds_addr(const char *p) { return (uint32_t)(uintptr_t)(AS3 const char *)p; }
 
@@ -230,6 +235,143 @@ __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// Global rows, partial over one wave's 32 keys.  A global row attends every
+// position ([PP] §4.3).  The keys at the class positions of a wave's own rows
+// (rho + dil*(row0 .. row0+31)) form one block of a partition of [0, T) over
+// all waves of the head; the wave scores every global row against that block
+// and stores its softmax state (m, l and the unnormalised output), which
+// launch_global_combine merges.  The global query, key and value rows come
+// from qg, kg, vg when given.
+//
+// gp_load issues the loads right after the banded loop (K in the operand
+// layout, the block's V rows, and for d_h = 64 the first 32 global queries),
+// so that they arrive while the epilogue runs; gp_finish stages V through the
+// wave's output slice (drained by the wave's output stores; LDS operations of
+// one wave run in order) for the transposing reads and does the rest.  Rows
+// past the class end read the last row instead (those keys are masked, so
+// their P is 0 and their finite V adds nothing), and global columns past G
+// read position 0 (their results are not stored): every load is in bounds and
+// unconditional.
+template <int D>
+struct GlobalPart {
+  static constexpr int KS = D / 16;  // k-steps of S (16-byte operand loads per lane)
+  static constexpr int NV = D / 16;  // 16-byte chunks of the 32 V rows per lane
+  static constexpr bool EARLY_Q = D == 64;  // registers allow the queries too
+  bf16x8 kf[KS];
+  u32x4 vr[NV];
+  bf16x8 qf[KS];
+};
+
+template <int D, bool GPROJ>
+__device__ inline void gp_load_q(bf16x8 *qf, const FwdArgs &a, int b, int h, int pos) {
+  const uint16_t *qsrc = static_cast<const uint16_t *>(GPROJ ? a.qg : a.q);
+  const uint16_t *qr = qsrc + (long long)b * a.q_sb + (long long)pos * a.q_st + (long long)h * D;
+  const int lh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const U4 *>(qr + ks * 16 + lh * 8));
+}
+
+template <int D, bool GPROJ>
+__device__ inline void gp_load(GlobalPart<D> &g, const FwdArgs &a, const GlobalList &gl, int b, int h,
+                               int kvh, int rho, int dil, int n_cls, int row0) {
+  const int lane = threadIdx.x & 63, lq = lane & 31, lh = lane >> 5;
+  // the first global positions before the K, V loads, so that the query
+  // loads wait for this load only
+  const int pos0 = lq < a.G ? gl.idx[b * a.G + lq] : 0;
+  const uint16_t *ksrc = static_cast<const uint16_t *>(GPROJ ? a.kg : a.k);
+  const uint16_t *vsrc = static_cast<const uint16_t *>(GPROJ ? a.vg : a.v);
+  const long long kv_off = (long long)b * a.k_sb + (long long)kvh * a.k_sh;
+  const int last = n_cls - 1;
+  const uint16_t *kr = ksrc + kv_off + (rho + (long long)dil * min(row0 + lq, last)) * a.k_st;
+#pragma unroll
+  for (int ks = 0; ks < GlobalPart<D>::KS; ++ks)
+    g.kf[ks] = as_bf16x8(*reinterpret_cast<const U4 *>(kr + ks * 16 + lh * 8));
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < GlobalPart<D>::NV; ++i) {
+    const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
+    g.vr[i] = *reinterpret_cast<const u32x4 *>(vsrc + kv_off + (rho + (long long)dil * min(row0 + r, last)) * a.k_st + ch * 8);
+  }
+  if constexpr (GlobalPart<D>::EARLY_Q) gp_load_q<D, GPROJ>(g.qf, a, b, h, pos0);
+}
+
+template <int D, bool GPROJ>
+__device__ inline void gp_finish(GlobalPart<D> &g, const FwdArgs &a, const GlobalList &gl, char *vsl,
+                                 int b, int h, int rho, int dil, int n_cls, int row0) {
+  using Gm = Geo<D>;
+  constexpr int DB = D / 32, CPR = D / 8;
+  const int lane = threadIdx.x & 63, lq = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < GlobalPart<D>::NV; ++i) {
+    const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
+    *reinterpret_cast<u32x4 *>(vsl + r * Gm::ROWB + ((ch ^ swz_v<D>(r)) * 16)) = g.vr[i];
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  // V^T operand offsets, as in the banded loop
+  uint32_t vop[DB];
+  {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int hh = grp >> 1, dg = grp & 1;
+    const int row = 4 * hh + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int c = 4 * db + 2 * dg + ((sl >> 1) & 1);
+      vop[db] = row * Gm::ROWB + ((c ^ swz_v<D>(row)) * 16) + 8 * (sl & 1);
+    }
+  }
+  const int last = n_cls - 1;
+  const int blk = class_tile_base(a.T, dil, kRowsPerWave, rho) + row0 / kRowsPerWave;
+  for (int u0 = 0; u0 < a.G; u0 += 32) {
+    const int u = u0 + lq;
+    if (!GlobalPart<D>::EARLY_Q || u0 > 0) gp_load_q<D, GPROJ>(g.qf, a, b, h, u < a.G ? gl.idx[b * a.G + u] : 0);
+    f32x16 sg = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < GlobalPart<D>::KS; ++ks)
+      sg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g.kf[ks], g.qf[ks], sg, 0, 0, 0);
+    // element e holds key row0 + 8(e/4) + 4lh + e%4 for global row u
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (row0 + 8 * (e >> 2) + 4 * lh + (e & 3) > last) sg[e] = -INFINITY;
+      mx = fmaxf(mx, sg[e]);
+    }
+    const float mg = xhalf_max(mx) * a.sl2;  // finite: key row0 exists
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sg[e] = __builtin_amdgcn_exp2f(fmaf(sg[e], a.sl2, -mg));
+      rs += sg[e];
+    }
+    const float lg = xhalf_add(rs);
+    f32x16 og[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) og[db] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      U4 pw;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) pw.w[w] = pack_bf16(sg[8 * kk + 2 * w], sg[8 * kk + 2 * w + 1]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char *p0 = vsl + kk * 16 * Gm::ROWB + vop[db];
+        og[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read8(p0, p0 + 8 * Gm::ROWB), as_bf16x8(pw),
+                                                         og[db], 0, 0, 0);
+      }
+    }
+    if (u < a.G) {
+      float *dst = a.gws + ((((long long)b * a.Hq + h) * a.G + u) * a.gnb + blk) * (D + 4);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<float4 *>(dst + db * 32 + 8 * g4 + 4 * lh) =
+              make_float4(og[db][4 * g4], og[db][4 * g4 + 1], og[db][4 * g4 + 2], og[db][4 * g4 + 3]);
+      if (lh == 0) *reinterpret_cast<float2 *>(dst + D) = make_float2(mg, lg);
+    }
+  }
+}
+
 // ---- the kernel ------------------------------------------------------------------
 
 template <int N>
@@ -250,7 +392,8 @@ constexpr float kLazy = 8.f;
 // MODE: kCausal, kSymmetric, kRing, kCausalSink, kSymmetricProj or kCausalDil
 // (FwdMode).
 template <int D, int MODE, int NW>
-__global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
+__global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
+                                      : (12 / NW) > 0 ? 12 / NW : 1) void fwd_kernel(
     const FwdArgs a, const GlobalList gl) {
   constexpr bool GPROJ = MODE == kSymmetricProj;  // separate global projections
   constexpr bool SYM = MODE == kSymmetric || GPROJ;
@@ -268,7 +411,10 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   constexpr int NST = SYM ? SWA_SYM_STAGES : 2;
   constexpr int OST_B = NW * kRowsPerWave * D * 2;
   constexpr int SMEM_B = (NST * STAGE_B > OST_B) ? NST * STAGE_B : OST_B;
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM_B];
+  // symmetric mode: K rows then V rows of the (at most kValuGlobals) global
+  // keys, staged once for the after-the-band pass
+  constexpr int GKV_B = MODE == kSymmetric ? 2 * kValuGlobals * Gm::ROWB : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_B + GKV_B];
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
   constexpr int BN = Gm::BN;     // keys per tile
@@ -345,6 +491,19 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   const uint16_t *kbase = kg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   const uint16_t *vbase = vg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   const int n_keyrows = RING ? a.S : n_cls;  // key rows of this (batch, head)
+
+  // -------- global keys of symmetric mode -> LDS (read after the band)
+  char *const gkv = smem + SMEM_B;
+  if constexpr (MODE == kSymmetric) {
+    constexpr int CPR = D / 8;
+    for (int i = tid; i < a.G * 2 * CPR; i += 64 * NW) {
+      const int u = i / (2 * CPR), isv = (i / CPR) & 1, ch = i % CPR;
+      const long long pos = gl.idx[b * a.G + u];
+      const uint16_t *src = (isv ? vbase : kbase) + pos * a.k_st + ch * 8;
+      *reinterpret_cast<U4 *>(gkv + (isv * kValuGlobals + u) * Gm::ROWB + ch * 16) =
+          *reinterpret_cast<const U4 *>(src);
+    }
+  }
 
   // -------- Q (B operand of S^T = K Q^T): lane holds row lq, columns 16ks + 8lh .. +7
   bf16x8 qf[KS_QK];
@@ -715,12 +874,16 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
           }
         return;
       }
+      // one unsigned compare per element: c in [lo, hi] iff c - lo <= hi - lo
+      // (an empty range moves lo out of reach)
+      const int lo2 = hi >= lo ? lo : (1 << 30);
+      const uint32_t span = hi >= lo ? (uint32_t)(hi - lo) : 0u;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
-          if (c < lo || c > hi) sv[kb][e] = -INFINITY;
+          if ((uint32_t)(c - lo2) > span) sv[kb][e] = -INFINITY;
         }
       return;
     }
@@ -791,9 +954,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
   // product through the partner lane; the state (m, l, O) is updated as for a
   // tile of one key, with P in fp32.  `take` drops keys the band already
   // counted (and rows past the end).
-  auto extra_key = [&](int key_pos, bool take) {
-    const long long kv_row = ((long long)b * a.k_sb + (long long)kvh * a.k_sh + (long long)key_pos * a.k_st) * 2;
-    const char *kr = reinterpret_cast<const char *>(kg) + kv_row;
+  auto extra_key = [&](const char *kr, const char *vr, bool take) {
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS_QK; ++ks) {
@@ -810,7 +971,6 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float pg = take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f;
     l_run += pg;
-    const char *vr = reinterpret_cast<const char *>(vg) + kv_row;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -828,7 +988,8 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       const int i_abs = rho + dil * my_row;
       for (int u = 0; u < a.G; ++u) {
         const int g = gl.idx[b * a.G + u];
-        extra_key(g, my_row < n_cls && !dilated_in(i_abs, g, a.W, dil));
+        extra_key(gkv + u * Gm::ROWB, gkv + (kValuGlobals + u) * Gm::ROWB,
+                  my_row < n_cls && !dilated_in(i_abs, g, a.W, dil));
       }
     }
   }
@@ -836,10 +997,19 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     // sink tokens s < n_sink before the row's window (s <= t - W); those
     // inside it were counted by the band
     if (has_rows)
-      for (int sk = 0; sk < a.n_sink; ++sk) extra_key(sk, my_row < n_cls && sk <= my_row - a.W);
+      for (int sk = 0; sk < a.n_sink; ++sk) {
+        const char *kr = reinterpret_cast<const char *>(kbase + (long long)sk * a.k_st);
+        const char *vr = reinterpret_cast<const char *>(vbase + (long long)sk * a.k_st);
+        extra_key(kr, vr, my_row < n_cls && sk <= my_row - a.W);
+      }
   }
+  // global rows: start this wave's loads now (see gp_load)
+  GlobalPart<D> gpart;
+  const bool gp_on = SYM && a.gws != nullptr && row0 < n_cls;
+  if constexpr (SYM)
+    if (gp_on) gp_load<D, GPROJ>(gpart, a, gl, b, h, kvh, rho, dil, n_cls, row0);
   // other waves may still read the last stage, which the output staging reuses
-  __syncthreads();
+  lds_barrier();
 
   // -------- epilogue: normalise, stage rows through LDS, coalesced stores
   // With a sink score z (natural-log units) the denominator gains exp(z): in
@@ -877,7 +1047,7 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
     const float lse = lse_l2 * 0.69314718055994531f;
     a.lse[((long long)b * a.Hq + h) * a.T + t_abs] = lse;
   }
-  __syncthreads();
+  lds_barrier();
   uint16_t *og = static_cast<uint16_t *>(a.o);
   constexpr int LPR = D / 8;             // lanes per row (16 B each)
   constexpr int RPI = 64 / LPR;          // rows per wave instruction
@@ -892,9 +1062,79 @@ __global__ __launch_bounds__(64 * NW, (12 / NW) > 0 ? 12 / NW : 1) void fwd_kern
       *reinterpret_cast<U4 *>(og + (long long)b * a.q_sb + t_abs * a.q_st + (long long)h * D + c * 8) = u;
     }
   }
+
+  // -------- global rows: partial over this wave's 32 keys
+  if constexpr (SYM)
+    if (gp_on) gp_finish<D, GPROJ>(gpart, a, gl, smem + wave * kRowsPerWave * D * 2, b, h, rho, dil, n_cls, row0);
+}
+
+// Global rows: merge the per-block states of launch_fwd_bf16's symmetric pass.
+// With M = max m_k (log2 units): o = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,
+// lse = (M + log2 L) ln 2.  A record's D outputs are read as D/4 float4 by as
+// many lanes, so one pass of the workgroup covers 1024/D records and all its
+// loads are independent.
+template <int D>
+__global__ __launch_bounds__(256) void global_combine_kernel(const FwdArgs a, const GlobalList gl) {
+  constexpr int PS = D + 4;      // floats per record
+  constexpr int LPR = D / 4;     // lanes per record
+  constexpr int RPP = 256 / LPR; // records per pass
+  __shared__ float s_m[4];
+  __shared__ float s_l[RPP];
+  __shared__ float4 s_o[RPP][LPR];
+  const int u = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid % LPR, j = tid / LPR;
+  const int nb = class_tiles(a.T, a.dil[h], kRowsPerWave);
+  const float *ws = a.gws + (((long long)b * a.Hq + h) * a.G + u) * a.gnb * PS;
+  float mloc = -INFINITY;
+  for (int k = tid; k < nb; k += 256) mloc = fmaxf(mloc, ws[(long long)k * PS + D]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, x));
+  if (lane == 0) s_m[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int k = j; k < nb; k += RPP) {
+    const float *rec = ws + (long long)k * PS;
+    const float2 ml = *reinterpret_cast<const float2 *>(rec + D);
+    const float4 x = *reinterpret_cast<const float4 *>(rec + 4 * c);
+    const float sc = __builtin_amdgcn_exp2f(ml.x - M);
+    L = fmaf(sc, ml.y, L);
+    o.x = fmaf(sc, x.x, o.x);
+    o.y = fmaf(sc, x.y, o.y);
+    o.z = fmaf(sc, x.z, o.z);
+    o.w = fmaf(sc, x.w, o.w);
+  }
+  s_o[j][c] = o;
+  if (c == 0) s_l[j] = L;
+  __syncthreads();
+  if (tid < D) {
+    float Lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+      Lt += s_l[i];
+      ot += reinterpret_cast<const float *>(&s_o[i][0])[tid];
+    }
+    const long long pos = gl.idx[b * a.G + u];
+    const __bf16 hv = (__bf16)(Lt > 0.f ? ot / Lt : 0.f);
+    static_cast<uint16_t *>(a.o)[(long long)b * a.q_sb + pos * a.q_st + (long long)h * D + tid] =
+        __builtin_bit_cast(uint16_t, hv);
+    if (a.lse && tid == 0)
+      a.lse[((long long)b * a.Hq + h) * a.T + pos] =
+          Lt > 0.f ? (M + __log2f(Lt)) * 0.69314718055994531f : -INFINITY;
+  }
 }
 
 }  // namespace
+
+hipError_t launch_global_combine(const FwdArgs &a, int D, const GlobalList *gl, hipStream_t st) {
+  const dim3 grid(a.G, a.Hq, a.B);
+  if (D == 128) hipLaunchKernelGGL((global_combine_kernel<128>), grid, dim3(256), 0, st, a, *gl);
+  else hipLaunchKernelGGL((global_combine_kernel<64>), grid, dim3(256), 0, st, a, *gl);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st) {

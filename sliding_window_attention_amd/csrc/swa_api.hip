@@ -9,6 +9,7 @@
 // [PP] "Sliding Window Attention: From Local Windows to Global Context" (prathamp.com);
 // [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai).
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -64,6 +65,27 @@ int chunk_for(bool f32, int n_keys, int S) {
 }
 
 swa_status hip_status(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_HIP; }
+
+// Longformer global rows on the bf16 path.  Either the banded kernel leaves a
+// partial softmax state per (global row, 32-key block of class positions) and
+// launch_global_combine merges them, or a split-KV pass recomputes the rows
+// from K and V.  The first needs lf_block_bytes and is taken whenever the
+// workspace holds it; swa_longformer_workspace_size covers it for every head
+// dilation up to kBlockMaxDil.  The second needs only lf_split_bytes.
+constexpr int kBlockMaxDil = 16;
+size_t lf_split_bytes(int B, int T, int H, int d_h, int G) {
+  const int S = splits_for(true, (long long)B * H, T);
+  return (size_t)B * H * G * S * (d_h + 2) * sizeof(float);
+}
+size_t lf_block_bytes(int B, int H, int d_h, int G, int n_blocks) {
+  return (size_t)B * H * G * n_blocks * (d_h + 4) * sizeof(float);
+}
+// Most 32-key blocks any head with dilation <= kBlockMaxDil has.
+int lf_block_cap(int T) {
+  int m = 0;
+  for (int d = 1; d <= kBlockMaxDil; ++d) m = std::max(m, class_tiles(T, d, kRowsPerWave));
+  return m;
+}
 
 }  // namespace
 }  // namespace swa
@@ -443,8 +465,8 @@ swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
 size_t swa_longformer_workspace_size(int B, int T, int H, int d_h, int G) {
   if (B < 1 || T < 1 || H < 1 || G < 0 || !d_ok(d_h)) return 0;
   if (G == 0) return 0;
-  const int S = splits_for(true, (long long)B * H, T);
-  return (size_t)B * H * G * S * (d_h + 2) * sizeof(float);
+  return std::max(swa::lf_split_bytes(B, T, H, d_h, G),
+                  swa::lf_block_bytes(B, H, d_h, G, swa::lf_block_cap(T)));
 }
 
 }  // extern "C"
@@ -477,7 +499,7 @@ swa_status longformer_impl(swa_dtype dt, const void *q, const void *k, const voi
       if (x < 0 || x >= T || (g > 0 && x <= global_idx[b * G + g - 1])) return SWA_ERR_INVALID;
     }
   if (!d_ok(d_h) || H > kMaxHeadsLF || (long long)B * G > kMaxGlobalsLF) return SWA_ERR_UNSUPPORTED;
-  const size_t need = (dt == SWA_F32) ? 0 : swa_longformer_workspace_size(B, T, H, d_h, G);
+  const size_t need = (dt == SWA_F32 || G == 0) ? 0 : lf_split_bytes(B, T, H, d_h, G);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SWA_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return SWA_ERR_INVALID;
 
@@ -526,8 +548,17 @@ swa_status longformer_impl(swa_dtype dt, const void *q, const void *k, const voi
   if (dt == SWA_F32)
     return hip_status(launch_fwd_f32(a, gproj ? kSymmetricProj : kSymmetric, d_h, &gl, st));
 
+  if (G > 0) {
+    int nb = 0;
+    for (int h = 0; h < H; ++h) nb = std::max(nb, class_tiles(T, a.dil[h], kRowsPerWave));
+    if (workspace_bytes >= lf_block_bytes(B, H, d_h, G, nb)) {
+      a.gws = static_cast<float *>(workspace);
+      a.gnb = nb;
+    }
+  }
   hipError_t e = launch_fwd_bf16(a, gtile ? kSymmetricProj : kSymmetric, d_h, &gl, st);
   if (e != hipSuccess || G == 0) return hip_status(e);
+  if (a.gws) return hip_status(launch_global_combine(a, d_h, &gl, st));
   // Global rows attend every position: split-KV over all T keys, written after
   // (stream order) the local pass, replacing those rows.  With separate
   // projections they read qg against kg, vg.

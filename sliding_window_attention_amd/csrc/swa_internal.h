@@ -88,6 +88,12 @@ __host__ __device__ inline int class_tiles(int n, int dil, int BM) {
   const ClassSplit c = class_split(n, dil);
   return c.rem * ceil_div(c.q + 1, BM) + (dil - c.rem) * ceil_div(c.q, BM);
 }
+// First tile index of class rho in the enumeration above (classes in order).
+__host__ __device__ inline int class_tile_base(int n, int dil, int BM, int rho) {
+  const ClassSplit c = class_split(n, dil);
+  const int c1 = ceil_div(c.q + 1, BM), c0 = ceil_div(c.q, BM);
+  return rho < c.rem ? rho * c1 : c.rem * c1 + (rho - c.rem) * c0;
+}
 // Inverse of the enumeration above: tile index -> (class, tile within class).
 __host__ __device__ inline void class_tile_decode(int n, int dil, int BM, int idx, int *rho, int *tile) {
   const ClassSplit c = class_split(n, dil);
@@ -189,6 +195,12 @@ struct FwdArgs {
   const float *sink_logit;   // [H_q] per-head sink score in the denominator, or null
   // symmetric mode: separate global projections (null = shared with q, k, v)
   const void *qg, *kg, *vg;
+  // symmetric mode, global rows (bf16): partial softmax states of every global
+  // row over each 32-key block of class positions, [B][H][G][gnb] records of
+  // D + 4 floats (D unnormalised outputs, m in log2 units, l); null = the
+  // global rows are computed by the split-KV pass instead
+  float *gws;
+  int gnb;  // record slots per (batch, head, global row): max over heads of the blocks
   // rotary positions applied to q in registers (causal modes): the pair
   // (x_i, x_{i+D/2}) of a row at position p turns by p * rope_rev0 * rope_step^i
   // revolutions (rope_rev0 = 1 / 2pi, rope_step = base^(-2/D))
@@ -245,6 +257,9 @@ struct SplitArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st);
+// Merges the per-block partial states of the global rows (FwdArgs::gws) into
+// their output rows and lse.
+hipError_t launch_global_combine(const FwdArgs &a, int D, const GlobalList *gl, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                           hipStream_t st);
 hipError_t launch_split(const SplitArgs &a, bool decode, bool f32, int D, const GlobalList *gl,

@@ -107,6 +107,21 @@ def test_longformer_validation():
     assert bd.lib().swa_longformer_workspace_size(2, 64, 3, 64, 0) == 0
 
 
+def _class_blocks(T, dil, n=32):
+    """32-key blocks over the residue classes of one head: sum over classes of
+    ceil(class length / 32)."""
+    return sum(-(-len(range(rho, T, dil)) // n) for rho in range(dil))
+
+
+@pytest.mark.parametrize("B,T,H,D,G", [(2, 64, 3, 64, 2), (8, 4096, 12, 64, 2), (1, 90, 2, 128, 5),
+                                       (3, 1000, 4, 128, 40)])
+def test_longformer_workspace_holds_block_states(B, T, H, D, G):
+    # the reported size holds one record of D + 4 floats per (batch, head,
+    # global row, 32-key block) for every head dilation up to 16
+    cap = max(_class_blocks(T, d) for d in range(1, 17))
+    assert bd.lib().swa_longformer_workspace_size(B, T, H, D, G) >= B * H * G * cap * (D + 4) * 4
+
+
 def _lfp(qg=P, kg=P, vg=P, **kw):
     a = dict(dt=0, B=2, T=64, H=3, D=64, r=4, sc=0.1, G=2)
     a.update(kw)

@@ -61,6 +61,41 @@ def test_longformer_f32(case):
     assert max_err(lse, rl) <= TOL_LSE_F32
 
 
+def _class_blocks(T, dil, n=32):
+    return sum(-(-len(range(rho, T, dil)) // n) for rho in range(dil))
+
+
+# The bf16 global rows come from per-block partial states when the workspace
+# holds them, else from a split-KV pass: both against the oracle and each other.
+@pytest.mark.parametrize("case", [
+    (2, 300, 4, 64, 20, [1, 2, 3, 1], [[0, 77], [5, 299]]),
+    (1, 129, 2, 128, 63, [4, 1], [[3, 64, 65, 100]]),
+    (1, 300, 2, 64, 9, [1, 3], [list(range(0, 300, 7))]),
+], ids=["d64", "d128", "43globals"])
+def test_longformer_global_rows_both_paths(case):
+    B, T, H, D, r, dil, gl = case
+    c = inp.LongformerCase(B=B, T=T, H=H, D=D, r=r, dilation=dil, globals_=gl[0], dtype="bf16",
+                           seed=T + 11 * H)
+    q, k, v, dl, _ = inp.longformer_inputs(c)
+    g = np.repeat(np.asarray(gl, dtype=np.int32).reshape(len(gl), -1), B // len(gl), axis=0)
+    G = g.shape[1]
+    nb = max(_class_blocks(T, d) for d in dl)
+    block_bytes = B * H * G * nb * (D + 4) * 4
+    banner(f"longformer global-row paths {case[:5]} G={G}")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ws_full = torch.empty(bd.longformer_workspace_size(B, T, H, D, G), dtype=torch.uint8, device="cuda")
+    ws_small = torch.empty(block_bytes - 256, dtype=torch.uint8, device="cuda")
+    o1, l1 = bd.longformer(qd, kd, vd, r, dl, g, workspace=ws_full, return_lse=True)
+    o2, l2 = bd.longformer(qd, kd, vd, r, dl, g, workspace=ws_small, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.swa_longformer(inp.widen(q), inp.widen(k), inp.widen(v), r, dl, g)
+    for o, lse in ((o1, l1), (o2, l2)):
+        assert max_err(host(o), ro) <= TOL_BF16
+        assert max_err(host(lse), rl) <= TOL_LSE_BF16
+    rows = g[0]
+    assert max_err(host(o1)[:, rows], host(o2)[:, rows]) <= TOL_BF16
+
+
 # B, T, H, D, r, dilation, globals (separate global projections)
 PROJ = [
     (1, 16, 2, 64, 2, [1, 2], [[0, 8]]),
