@@ -453,10 +453,15 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // find the head (group): head_off[g] <= rem < head_off[g+1]
     int lo = 0, hi = (SYM ? a.Hq : a.n_hg) - 1;
     while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
+      const int mid = uni((lo + hi + 1) >> 1);
       if (a.head_off[mid] <= rem) lo = mid; else hi = mid - 1;
     }
-    dil = a.dil[lo];
+    lo = uni(lo);
+    {
+      // the 16-bit entry from its 32-bit word, so the load is a scalar one
+      const uint32_t w = reinterpret_cast<const uint32_t *>(a.dil)[lo >> 1];
+      dil = (lo & 1) ? (int)(w >> 16) : (int)(w & 0xffffu);
+    }
     int tile;
     class_tile_decode(a.T, dil, a.BM, rem - a.head_off[lo], &rho, &tile);
     n_cls = class_len(class_split(a.T, dil), rho);
@@ -492,7 +497,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   const uint16_t *vbase = vg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   const int n_keyrows = RING ? a.S : n_cls;  // key rows of this (batch, head)
 
-  // -------- global keys of symmetric mode -> LDS (read after the band)
+  // -------- global keys of symmetric mode -> LDS (read after the band; the
+  // first tile step's barrier publishes them to the other waves)
   char *const gkv = smem + SMEM_B;
   if constexpr (MODE == kSymmetric) {
     constexpr int CPR = D / 8;
@@ -504,6 +510,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
           *reinterpret_cast<const U4 *>(src);
     }
   }
+
+  // ring mode: this lane's query position, loaded ahead of Q so that waiting
+  // for it does not wait for Q
+  int q_pos_ld = 0;
+  if constexpr (RING)
+    if (row0 + lq < n_cls) q_pos_ld = a.q_pos[(long long)b * a.T + row0 + lq];
 
   // -------- Q (B operand of S^T = K Q^T): lane holds row lq, columns 16ks + 8lh .. +7
   bf16x8 qf[KS_QK];
@@ -517,35 +529,6 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       if (r < n_cls) u = *reinterpret_cast<const U4 *>(qp + ks * 16 + lh * 8);
       qf[ks] = as_bf16x8(u);
     }
-    if constexpr (!SYM && !RING) {
-      if (a.rope) {
-        // Rotary positions, rotate-half pairs (c, c + D/2): this lane holds
-        // columns c = 16ks + 8lh + e, whose partners sit in qf[ks + KS_QK/2].
-        // The angle of pair c is p * base^(-2c/D) (revolutions in float64).
-        const double p = (double)rho + (double)dil * (double)r;
-        const double s1 = a.rope_step, s16 = rope_pow(s1, 16);
-        double rk = a.rope_rev0 * rope_pow(s1, 8 * lh);
-#pragma unroll
-        for (int ks = 0; ks < KS_QK / 2; ++ks) {
-          double ri = rk;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f = rope_frac(p, ri);
-            const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
-            const float x = (float)qf[ks][e], y = (float)qf[ks + KS_QK / 2][e];
-            qf[ks][e] = (__bf16)(x * cs - y * sn);
-            qf[ks + KS_QK / 2][e] = (__bf16)(y * cs + x * sn);
-            ri *= s1;
-          }
-          rk *= s16;
-        }
-      }
-    }
-    // Make the compiler wait for the Q loads here, before the tile loop: the
-    // copies issued in the loop are invisible to its counter tracking, so a
-    // wait for Q placed inside the loop would also stall on them.
-#pragma unroll
-    for (int ks = 0; ks < KS_QK; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   // -------- schedule
@@ -796,7 +779,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   int my_pos = 0, pos_lo = 0, pos_hi = 0;
   if constexpr (RING) {
     const bool ok = my_row < n_cls;
-    my_pos = ok ? a.q_pos[(long long)b * a.T + my_row] : 0;
+    my_pos = q_pos_ld;
     int lo = ok ? my_pos : INT_MAX, hi = ok ? my_pos : INT_MIN;
 #pragma unroll
     for (int x = 16; x >= 1; x >>= 1) {
@@ -939,6 +922,36 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
     if (p < n_tiles) issue(p, a_s0 + (uint32_t)(p * STAGE_B));
+  if constexpr (!SYM && !RING) {
+    if (a.rope) {
+      // Rotary positions, rotate-half pairs (c, c + D/2): this lane holds
+      // columns c = 16ks + 8lh + e, whose partners sit in qf[ks + KS_QK/2].
+      // The angle of pair c is p * base^(-2c/D) (revolutions in float64).
+      const double p = (double)rho + (double)dil * (double)(row0 + lq);
+      const double s1 = a.rope_step, s16 = rope_pow(s1, 16);
+      double rk = a.rope_rev0 * rope_pow(s1, 8 * lh);
+#pragma unroll
+      for (int ks = 0; ks < KS_QK / 2; ++ks) {
+        double ri = rk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = rope_frac(p, ri);
+          const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+          const float x = (float)qf[ks][e], y = (float)qf[ks + KS_QK / 2][e];
+          qf[ks][e] = (__bf16)(x * cs - y * sn);
+          qf[ks + KS_QK / 2][e] = (__bf16)(y * cs + x * sn);
+          ri *= s1;
+        }
+        rk *= s16;
+      }
+    }
+  }
+  // Make the compiler wait for the Q loads here, after the first copies are
+  // issued (so the two latencies overlap) and before the tile loop: the copies
+  // are invisible to its counter tracking, so a wait for Q placed inside the
+  // loop would also stall on later copies.
+#pragma unroll
+  for (int ks = 0; ks < KS_QK; ++ks) asm volatile("" ::"v"(qf[ks]));
   static_assert(NST >= 2 && NST <= 4, "two to four stages");
   for (int j = 0; j < n_tiles; j += NST) {
     step(j, IntC<0>{});
