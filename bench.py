@@ -11,7 +11,9 @@ inside the call) are reported in "extra".
 Timing: inputs resident in HBM, W untimed warm-up launches, then K launches
 bracketed by torch.cuda.synchronize() and HIP events recorded on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
-the library).
+the library).  A separate pass then times up to 50 launches one by one for the
+median / min / p90 ("launch_ms"); "inputs" gives the generator, seed and the
+SHA-256 of the headline's host inputs.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--only prefill|local|decode|longformer|chunk|sinks|dilated|rope]
@@ -90,7 +92,14 @@ def measured_traffic(kernel_key):
                 write_bytes=k["write_bytes"])
 
 
-def time_launches(fn, steps, warmup):
+LAUNCH_STATS = {}
+
+
+def time_launches(fn, steps, warmup, name=None):
+    """Average ms per launch over `steps` back-to-back launches (one event pair
+    around all of them).  With `name`, a second, separate pass brackets each of
+    up to 50 launches with its own event pair and records median / min / p90
+    in LAUNCH_STATS[name]; it is not part of the timed average."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -104,17 +113,42 @@ def time_launches(fn, steps, warmup):
     e1.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if name is not None:
+        n = min(steps, 50)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record(s)
+            fn()
+            b.record(s)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        LAUNCH_STATS[name] = dict(n=n, median=round(float(np.median(t)), 4),
+                                  min=round(float(t.min()), 4),
+                                  p90=round(float(np.quantile(t, 0.9)), 4))
     return e0.elapsed_time(e1) / steps, wall
 
 
-def bench_prefill(c, steps, warmup):
-    q, k, v = (x.cuda() for x in inp.prefill_inputs(c))
+def inputs_sha256(*tensors):
+    """SHA-256 over the raw bytes of the generated host inputs, in order."""
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes() if t.dtype != torch.bfloat16
+                 else t.contiguous().view(torch.int16).numpy().tobytes())
+    return h.hexdigest()
+
+
+def bench_prefill(c, steps, warmup, name=None):
+    qh, kh, vh = inp.prefill_inputs(c)
+    sha = inputs_sha256(qh, kh, vh)
+    q, k, v = qh.cuda(), kh.cuda(), vh.cuda()
+    del qh, kh, vh
     o = torch.empty_like(q)
-    ms, _ = time_launches(lambda: bd.prefill(q, k, v, c.W, out=o), steps, warmup)
+    ms, _ = time_launches(lambda: bd.prefill(q, k, v, c.W, out=o), steps, warmup, name)
     flops = 4.0 * c.D * c.Hq * c.B * causal_pairs(c.T, c.W)
     nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel())
     tflops = flops / (ms * 1e-3) / 1e12
-    return dict(ms=ms, tflops=tflops, flops=flops, bytes=nbytes)
+    return dict(ms=ms, tflops=tflops, flops=flops, bytes=nbytes, sha256=sha)
 
 
 def causal_sink_pairs(T, W, n_sink):
@@ -165,7 +199,8 @@ def bench_decode(c, steps, warmup):
     o = torch.empty_like(q)
     ws = torch.empty(bd.decode_workspace_size(c.B, c.Hq, c.Hkv, c.W, c.D), dtype=torch.uint8,
                      device="cuda")
-    ms, _ = time_launches(lambda: bd.decode(q, kc, vc, sp, cur, out=o, workspace=ws), steps, warmup)
+    ms, _ = time_launches(lambda: bd.decode(q, kc, vc, sp, cur, out=o, workspace=ws), steps, warmup,
+                          "decode")
     nbytes = 2 * (q.numel() + kc.numel() + vc.numel() + o.numel()) + 4 * (sp.numel() + cur.numel())
     return dict(ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, bytes=nbytes)
 
@@ -177,7 +212,7 @@ def bench_longformer(c, steps, warmup):
     ws = torch.empty(max(1, bd.longformer_workspace_size(c.B, c.T, c.H, c.D, g.shape[1])),
                      dtype=torch.uint8, device="cuda")
     ms, _ = time_launches(lambda: bd.longformer(q, k, v, c.r, dl, g, out=o, workspace=ws),
-                          steps, warmup)
+                          steps, warmup, "longformer")
     pairs = c.B * longformer_pairs(c.T, c.r, c.dilation, c.globals_)
     flops = 4.0 * c.D * pairs
     nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel())
@@ -257,7 +292,7 @@ def main():
     c2 = inp.C2
     main_r = None
     if args.only in ("all", "prefill"):
-        main_r = bench_prefill(c2, args.steps, args.warmup)
+        main_r = bench_prefill(c2, args.steps, args.warmup, "headline")
     extra = {}
     if args.only in ("all", "local"):
         r3 = bench_prefill(inp.C3, max(5, args.steps // 2), args.warmup)
@@ -271,14 +306,16 @@ def main():
             workload="ring decode B=64 W=4096 Hq=32 Hkv=8 d_h=128 bf16, cur_pos in [4096, 32768)",
             value=round(r4["gbs"], 1), unit="GB/s", ms=round(r4["ms"], 4),
             frac_hbm_peak=round(r4["gbs"] / PEAK_HBM_GBS, 4), bytes=r4["bytes"],
-            traffic=measured_traffic("split_mfma_kernel<128, 4, true, 4>@131072"))
+            traffic=measured_traffic("split_mfma_kernel<128, 4, true, 4>@131072"),
+            launch_ms=LAUNCH_STATS.get("decode"))
     if args.only in ("all", "longformer"):
         r5 = bench_longformer(inp.C5, max(20, args.steps), args.warmup)
         extra["longformer"] = dict(
             workload="Longformer B=8 T=4096 H=12 d_h=64 r=256, dilation 2 on heads 8-11, globals {0,8}",
             value=round(r5["tflops"], 2), unit="TFLOP/s", ms=round(r5["ms"], 4),
             frac_of_roofline=round(r5["frac_of_roof"], 4), pairs=r5["pairs"],
-            traffic_local_pass=measured_traffic("fwd_kernel<64, 1, 4>@786432"))
+            traffic_local_pass=measured_traffic("fwd_kernel<64, 1, 4>@786432"),
+            launch_ms=LAUNCH_STATS.get("longformer"))
 
     if args.only in ("all", "chunk"):
         c6 = inp.C6
@@ -348,6 +385,9 @@ def main():
                      "algorithmic_flop_per_launch": main_r["flops"],
                      "algorithmic_bytes_per_launch": main_r["bytes"]},
         "cpu_baseline": cpu,
+        "launch_ms": LAUNCH_STATS.get("headline"),
+        "inputs": {"generator": "numpy PCG64 standard_normal float32, rounded to bf16 (RNE)",
+                   "seed": c2.seed, "sha256_q_k_v": main_r["sha256"]},
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
