@@ -38,6 +38,9 @@
 // added after the band, one key at a time in registers.  Symmetric
 // mode may take separate global projections ([PP] §5.2): every global key of a
 // local row then comes from K_g, V_g (the window tiles drop global positions).
+// The global rows themselves (which attend every position, [PP] §4.3) are
+// computed from per-block partial states each wave of symmetric mode leaves
+// after its own rows (gp_load / gp_finish) and merged by global_combine_kernel.
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [PP] "Sliding Window Attention: From Local Windows to Global Context"
@@ -243,9 +246,10 @@ __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
 // launch_global_combine merges.  The global query, key and value rows come
 // from qg, kg, vg when given.
 //
-// gp_load issues the loads right after the banded loop (K in the operand
-// layout, the block's V rows, and for d_h = 64 the first 32 global queries),
-// so that they arrive while the epilogue runs; gp_finish stages V through the
+// gp_load issues the loads after the banded loop and the out-of-band keys,
+// before the epilogue (K in the operand layout, the block's V rows, and for
+// d_h = 64 the first 32 global queries), so that they arrive while the
+// epilogue runs; gp_finish stages V through the
 // wave's output slice (drained by the wave's output stores; LDS operations of
 // one wave run in order) for the transposing reads and does the rest.  Rows
 // past the class end read the last row instead (those keys are masked, so
