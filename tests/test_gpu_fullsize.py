@@ -14,9 +14,11 @@ from gpu_util import TOL_BF16, TOL_LSE_BF16, banner, dev, host, max_err
 pytestmark = pytest.mark.gpu
 
 
-def _sample_rows(T, W, seed, n_rand=8):
+def _sample_rows(T, W, seed, n_rand=32):
+    # the ramp's first rows, the rows around the first full window, the last
+    # rows, and seeded random rows
     rng = np.random.default_rng(seed)
-    rows = set(range(0, 12)) | set(range(max(0, W - 6), min(T, W + 6))) | set(range(T - 6, T))
+    rows = set(range(0, 32)) | set(range(max(0, W - 16), min(T, W + 16))) | set(range(T - 32, T))
     rows |= set(rng.integers(0, T, size=n_rand).tolist())
     return np.array(sorted(rows))
 
@@ -62,6 +64,21 @@ def test_longformer_fullsize_sampled():
     ro, rl = oracle.swa_longformer(inp.widen(q), inp.widen(k), inp.widen(v), c.r, dl, g, rows=rows)
     assert max_err(host(o[:, rows]), ro) <= TOL_BF16
     assert max_err(host(lse[:, :, rows]), rl) <= TOL_LSE_BF16
+
+
+def test_longformer_fullsize_all_outputs():
+    # every output (all batch rows, rows and heads, global rows included) of
+    # the full-size launch, against the oracle one batch row at a time
+    c = inp.C5
+    q, k, v, dl, g = inp.longformer_inputs(c)
+    banner(f"longformer full size, all outputs: B={c.B} T={c.T} H={c.H} r={c.r}")
+    o, lse = bd.longformer(dev(q), dev(k), dev(v), c.r, dl, g, return_lse=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = inp.widen(q), inp.widen(k), inp.widen(v)
+    for b in range(c.B):
+        ro, rl = oracle.swa_longformer(qn[b:b + 1], kn[b:b + 1], vn[b:b + 1], c.r, dl, g[b:b + 1])
+        assert max_err(host(o[b:b + 1]), ro) <= TOL_BF16, f"batch {b}"
+        assert max_err(host(lse[b:b + 1]), rl) <= TOL_LSE_BF16, f"lse batch {b}"
 
 
 # ---- every row at full size, q = 0 ----------------------------------------------
