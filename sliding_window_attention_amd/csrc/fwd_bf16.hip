@@ -417,7 +417,9 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   constexpr int SMEM_B = (NST * STAGE_B > OST_B) ? NST * STAGE_B : OST_B;
   // symmetric mode: K rows then V rows of the (at most kValuGlobals) global
   // keys, staged once for the after-the-band pass
-  constexpr int GKV_B = MODE == kSymmetric ? 2 * kValuGlobals * Gm::ROWB : 0;
+  // (causal sink mode: the K rows then V rows of the sink tokens, likewise)
+  constexpr int GKV_ROWS = MODE == kSymmetric ? kValuGlobals : MODE == kCausalSink ? kMaxSinks : 0;
+  constexpr int GKV_B = 2 * GKV_ROWS * Gm::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_B + GKV_B];
   constexpr int KS_QK = D / 16;  // k-steps of S = Q K^T
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
@@ -501,8 +503,9 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   const uint16_t *vbase = vg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   const int n_keyrows = RING ? a.S : n_cls;  // key rows of this (batch, head)
 
-  // -------- global keys of symmetric mode -> LDS (read after the band; the
-  // first tile step's barrier publishes them to the other waves)
+  // -------- global keys of symmetric mode, sink tokens of causal sink mode ->
+  // LDS (read after the band; the first tile step's barrier publishes them to
+  // the other waves)
   char *const gkv = smem + SMEM_B;
   if constexpr (MODE == kSymmetric) {
     constexpr int CPR = D / 8;
@@ -511,6 +514,17 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       const long long pos = gl.idx[b * a.G + u];
       const uint16_t *src = (isv ? vbase : kbase) + pos * a.k_st + ch * 8;
       *reinterpret_cast<U4 *>(gkv + (isv * kValuGlobals + u) * Gm::ROWB + ch * 16) =
+          *reinterpret_cast<const U4 *>(src);
+    }
+  }
+  // sink tokens that exist (positions below both n_sink and T)
+  const int n_sink = CSINK ? min(a.n_sink, n_cls) : 0;
+  if constexpr (CSINK) {
+    constexpr int CPR = D / 8;
+    for (int i = tid; i < n_sink * 2 * CPR; i += 64 * NW) {
+      const int sk = i / (2 * CPR), isv = (i / CPR) & 1, ch = i % CPR;
+      const uint16_t *src = (isv ? vbase : kbase) + (long long)sk * a.k_st + ch * 8;
+      *reinterpret_cast<U4 *>(gkv + (isv * kMaxSinks + sk) * Gm::ROWB + ch * 16) =
           *reinterpret_cast<const U4 *>(src);
     }
   }
@@ -1014,11 +1028,9 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // sink tokens s < n_sink before the row's window (s <= t - W); those
     // inside it were counted by the band
     if (has_rows)
-      for (int sk = 0; sk < a.n_sink; ++sk) {
-        const char *kr = reinterpret_cast<const char *>(kbase + (long long)sk * a.k_st);
-        const char *vr = reinterpret_cast<const char *>(vbase + (long long)sk * a.k_st);
-        extra_key(kr, vr, my_row < n_cls && sk <= my_row - a.W);
-      }
+      for (int sk = 0; sk < n_sink; ++sk)
+        extra_key(gkv + sk * Gm::ROWB, gkv + (kMaxSinks + sk) * Gm::ROWB,
+                  my_row < n_cls && sk <= my_row - a.W);
   }
   // global rows: start this wave's loads now (see gp_load)
   GlobalPart<D> gpart;

@@ -24,8 +24,10 @@ def _tols(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,T,W,Hq,Hkv,D,n_sink,logits", [
-    (2, 300, 64, 8, 2, 128, 4, True),     # sink tile after the window tiles
-    (1, 150, 100, 4, 4, 64, 32, False),   # key tile 0 inside the window range (union mask)
+    (2, 300, 64, 8, 2, 128, 4, True),     # sinks before the window of most rows
+    (1, 150, 100, 4, 4, 64, 32, False),   # sinks partly inside the window (counted once)
+    (1, 20, 8, 4, 2, 128, 32, True),      # more sink tokens than positions
+    (1, 40, 64, 2, 1, 64, 32, True),      # W > T: every sink already in the window
     (2, 200, 1, 4, 1, 128, 3, True),      # W = 1: self plus the sinks
     (2, 260, 40, 8, 4, 128, 5, True),     # two heads per K/V head: two row blocks per workgroup
     (1, 96, 50, 4, 2, 128, 0, True),      # sink scores only
