@@ -880,12 +880,20 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       const int lo2 = hi >= lo ? lo : (1 << 30);
       const uint32_t span = hi >= lo ? (uint32_t)(hi - lo) : 0u;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
+        if constexpr (KB > 1) {
+          // a 32-key block inside every row's window needs no mask
+          const int blk = (tr.lo + j) * (BN / 32) + kb;
+          const bool full = SYM ? sym_tile_full(row0, w_last, blk, 32, a.W, n_cls)
+                                : causal_tile_full(row0, w_last, blk, 32, a.W, n_cls);
+          if (full) continue;
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
           if ((uint32_t)(c - lo2) > span) sv[kb][e] = -INFINITY;
         }
+      }
       return;
     }
     if constexpr (!SYM) return;
