@@ -8,7 +8,8 @@ Longformer B=8 T=4096 r=256, chunked prefill of 512-token chunks over a ring
 cache, prefill with attention sinks, dilated prefill, prefill with RoPE applied
 inside the call) are reported in "extra".
 
-Timing: inputs resident in HBM, W untimed warm-up launches, then K launches
+Timing: inputs resident in HBM, W untimed warm-up launches (and at least
+50 ms of them), then K launches
 bracketed by torch.cuda.synchronize() and HIP events recorded on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
 the library).  A separate pass then times up to 50 launches one by one for the
@@ -100,8 +101,15 @@ def time_launches(fn, steps, warmup, name=None):
     around all of them).  With `name`, a second, separate pass brackets each of
     up to 50 launches with its own event pair and records median / min / p90
     in LAUNCH_STATS[name]; it is not part of the timed average."""
-    for _ in range(warmup):
+    # at least `warmup` launches and at least 50 ms of them, so that short
+    # kernels also reach the steady clock before the timed launches
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < warmup or time.perf_counter() - t_w < 0.05:
         fn()
+        n_w += 1
+        if n_w % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
