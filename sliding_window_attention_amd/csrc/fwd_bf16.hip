@@ -84,6 +84,33 @@ __device__ inline float xhalf_add(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Minimum and maximum of lo, hi over each half-wave (WHOLE: over the wave)
+// with cross-lane VALU moves: DPP inside rows of 16 lanes (lane ^ 1, lane ^ 2,
+// then the mirrored lane of the 8- and the 16-lane group), then
+// v_permlane16_swap (and v_permlane32_swap).  No LDS round trip, unlike a
+// general lane shuffle.
+template <bool WHOLE>
+__device__ inline void lane_minmax(int &lo, int &hi) {
+#define SWA_DPP_STEP(ctrl)                                                   \
+  lo = min(lo, __builtin_amdgcn_update_dpp(lo, lo, ctrl, 0xF, 0xF, false)); \
+  hi = max(hi, __builtin_amdgcn_update_dpp(hi, hi, ctrl, 0xF, 0xF, false));
+  SWA_DPP_STEP(0xB1)   // quad_perm [1, 0, 3, 2]
+  SWA_DPP_STEP(0x4E)   // quad_perm [2, 3, 0, 1]
+  SWA_DPP_STEP(0x141)  // row_half_mirror
+  SWA_DPP_STEP(0x140)  // row_mirror
+#undef SWA_DPP_STEP
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)lo, (uint32_t)lo, false, false);
+  auto b = __builtin_amdgcn_permlane16_swap((uint32_t)hi, (uint32_t)hi, false, false);
+  lo = min((int)a[0], (int)a[1]);
+  hi = max((int)b[0], (int)b[1]);
+  if constexpr (WHOLE) {
+    auto c = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
+    auto d = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
+    lo = min((int)c[0], (int)c[1]);
+    hi = max((int)d[0], (int)d[1]);
+  }
+}
+
 // ---- LDS layouts ---------------------------------------------------------------
 #define AS1 __attribute__((address_space(1)))
 #define AS3 __attribute__((address_space(3)))
@@ -210,6 +237,19 @@ __device__ inline void dma_dword(const char *gbase, uint32_t off, uint32_t lds) 
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(uni_u32(lds)), "s"(uni_ptr(gbase)), "v"(off));
+}
+
+// One 16-byte copy per lane from a full 64-bit address (no scalar base):
+// lane i's bytes land at LDS byte m0 + 16*i.
+__device__ inline void dma_addr(const void *src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(uni_u32(lds)), "v"(src));
 }
 
 // Wait until at most n of this wave's vector-memory operations are still in
@@ -504,28 +544,33 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   const int n_keyrows = RING ? a.S : n_cls;  // key rows of this (batch, head)
 
   // -------- global keys of symmetric mode, sink tokens of causal sink mode ->
-  // LDS (read after the band; the first tile step's barrier publishes them to
-  // the other waves)
+  // LDS: the K rows, then (GKV_ROWS rows further) the V rows, copied straight
+  // into LDS, RPI rows per wave instruction.  They are issued before every
+  // other load, so the first tile step's wait covers them and its barrier
+  // publishes them to the other waves; they are read after the band.  Rows
+  // past the last one repeat it (inside the GKV_ROWS-row regions).
   char *const gkv = smem + SMEM_B;
-  if constexpr (MODE == kSymmetric) {
-    constexpr int CPR = D / 8;
-    for (int i = tid; i < a.G * 2 * CPR; i += 64 * NW) {
-      const int u = i / (2 * CPR), isv = (i / CPR) & 1, ch = i % CPR;
-      const long long pos = gl.idx[b * a.G + u];
-      const uint16_t *src = (isv ? vbase : kbase) + pos * a.k_st + ch * 8;
-      *reinterpret_cast<U4 *>(gkv + (isv * kValuGlobals + u) * Gm::ROWB + ch * 16) =
-          *reinterpret_cast<const U4 *>(src);
-    }
-  }
   // sink tokens that exist (positions below both n_sink and T)
   const int n_sink = CSINK ? min(a.n_sink, n_cls) : 0;
-  if constexpr (CSINK) {
-    constexpr int CPR = D / 8;
-    for (int i = tid; i < n_sink * 2 * CPR; i += 64 * NW) {
-      const int sk = i / (2 * CPR), isv = (i / CPR) & 1, ch = i % CPR;
-      const uint16_t *src = (isv ? vbase : kbase) + (long long)sk * a.k_st + ch * 8;
-      *reinterpret_cast<U4 *>(gkv + (isv * kMaxSinks + sk) * Gm::ROWB + ch * 16) =
-          *reinterpret_cast<const U4 *>(src);
+  if constexpr (MODE == kSymmetric || CSINK) {
+    constexpr int RPI = Gm::RPI, CPR = D / 8;
+    const int n_rows = CSINK ? n_sink : a.G;
+    const int n_i = (n_rows + RPI - 1) / RPI;  // copies per tensor
+    const int sub = lane / CPR;                 // this lane's row in a copy
+    for (int i = wave; i < 2 * n_i; i += NW) {
+      const int isv = i >= n_i;
+      const int r0i = (isv ? i - n_i : i) * RPI;
+      int pos = min(r0i + sub, n_rows - 1);  // sinks: positions 0 .. n_sink-1
+      if constexpr (MODE == kSymmetric) {
+        // the global positions, read with wave-uniform indices
+#pragma unroll
+        for (int k = 0; k < RPI; ++k) {
+          const int pk = gl.idx[b * a.G + min(r0i + k, n_rows - 1)];
+          pos = sub == k ? pk : pos;
+        }
+      }
+      const uint16_t *src = (isv ? vbase : kbase) + (long long)pos * a.k_st + (lane % CPR) * 8;
+      dma_addr(src, lds_addr(gkv) + (uint32_t)((isv * GKV_ROWS + r0i) * Gm::ROWB));
     }
   }
 
@@ -799,11 +844,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     const bool ok = my_row < n_cls;
     my_pos = q_pos_ld;
     int lo = ok ? my_pos : INT_MAX, hi = ok ? my_pos : INT_MIN;
-#pragma unroll
-    for (int x = 16; x >= 1; x >>= 1) {
-      lo = min(lo, __shfl_xor(lo, x));
-      hi = max(hi, __shfl_xor(hi, x));
-    }
+    lane_minmax<false>(lo, hi);  // both half-waves hold the same 32 rows
     pos_lo = uni(lo);
     pos_hi = uni(hi);
     asm volatile("" ::"v"(my_pos));
@@ -820,11 +861,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
                       ((long long)sp > (long long)pos_lo - a.W || sp < a.n_sink);
     if (__builtin_amdgcn_ballot_w64(live) == 0) return 0;
     int lo = sp, hi = sp;
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) {
-      lo = min(lo, __shfl_xor(lo, x));
-      hi = max(hi, __shfl_xor(hi, x));
-    }
+    lane_minmax<(BN > 32)>(lo, hi);  // with 32 slots both half-waves hold them all
     const bool full = n_in == BN && uni(lo) >= 0 &&
                       (long long)uni(lo) > (long long)pos_hi - a.W && uni(hi) <= pos_lo;
     return full ? 1 : 2;
@@ -987,6 +1024,11 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     if constexpr (NST > 3)
       if (j + 3 < n_tiles) step(j + 3, IntC<3 % NST>{});
   }
+  if constexpr (MODE == kSymmetric || CSINK)
+    if (n_tiles == 0) {  // (workgroup-uniform) no tile step waited for the staged rows
+      wait_dma_keep(0);
+      __syncthreads();
+    }
   // Keys outside the band, one at a time in registers: the few global keys of
   // Longformer mode (at most kValuGlobals) and the sink tokens of causal mode.
   // Each lane holds half of its row's q and forms the other half's partial dot

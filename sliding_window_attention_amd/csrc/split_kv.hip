@@ -271,6 +271,22 @@ __device__ inline float xhalf_add(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Sum of x over the lanes that share lane % N (N = 8, 16 or 32): a butterfly
+// over lane ^ N, lane ^ 2N, ... with cross-lane VALU moves (DPP rotation by 8
+// inside rows of 16 lanes, v_permlane16_swap, v_permlane32_swap) instead of
+// LDS-routed shuffles.  Same pairs and order as the shuffle butterfly.
+template <int N>
+__device__ inline float lane_group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "butterfly from lane ^ 8, 16 or 32");
+  if constexpr (N == 8)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  if constexpr (N <= 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return xhalf_add(x);
+}
+
 __device__ inline uint32_t pack2_bf16(float a, float b) {
   bf16x2 v;
   v[0] = (__bf16)a;
@@ -503,10 +519,7 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
   for (int q = 0; q < QG; ++q)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float x = acc[q][e];
-#pragma unroll
-      for (int sft = TPR; sft < 64; sft <<= 1) x += __shfl_xor(x, sft);
-      acc[q][e] = x;
+      acc[q][e] = lane_group_sum<TPR>(acc[q][e]);
     }
   const long long base = ((long long)b * a.NKV + kvh) * a.NQ;
   if constexpr (NSW == 0) {
