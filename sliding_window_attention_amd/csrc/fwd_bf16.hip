@@ -10,9 +10,11 @@
 //
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in VGPRs (B)
 //   mask             only on tiles the schedule marks as partial
-//   online softmax   each lane owns one query row: the row max / sum over the
+//   online softmax   each lane owns one query row: the row max over the
 //                    32x32 accumulator is a 16-register reduction plus one
-//                    v_permlane32_swap with the partner half-wave
+//                    v_permlane32_swap with the partner half-wave; the row
+//                    sum stays split between the two half-waves (v_dot2 of
+//                    the packed P against ones) until the epilogue
 //   O^T += V^T P^T   P^T stays in VGPRs as the B operand; the V^T operand is
 //                    read from the row-major V tile with ds_read_b64_tr_b16
 //
@@ -780,21 +782,25 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // operands of the four PV k-steps
   auto exp_pack = [&](f32x16 *sv, U4 *pu) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sv[kb][e] = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], a.sl2, -m_use));
-        rs += sv[kb][e];
-      }
-    l_run += xhalf_add(rs);
+      for (int e = 0; e < 16; ++e) sv[kb][e] = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], a.sl2, -m_use));
 #pragma unroll
     for (int kk = 0; kk < PK; ++kk) {
       const int kb = kk >> 1, e0 = (kk & 1) * 8;
 #pragma unroll
       for (int w = 0; w < 4; ++w) pu[kk].w[w] = pack_bf16(sv[kb][e0 + 2 * w], sv[kb][e0 + 2 * w + 1]);
     }
+    // Row sum of the P the product uses (bf16 pairs, v_dot2 against ones,
+    // fp32 accumulation): this lane's keys only; the half-wave partner's
+    // share is added once, before the epilogue.
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int kk = 0; kk < PK; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu[kk].w[w]), ones, l_run, false);
   };
   // O^T += V^T P^T : key steps of 16
   auto pv = [&](const char *vs, const U4 *pu) {
@@ -1051,7 +1057,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     rescale(sg);
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float pg = take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f;
-    l_run += pg;
+    if (lh == 0) l_run += pg;  // l_run holds per-lane shares until the epilogue
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1094,6 +1100,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // With a sink score z (natural-log units) the denominator gains exp(z): in
   // the log2 domain of m, l that is 2^(z log2 e - m), taken against the larger
   // of m and z log2 e so neither side overflows.
+  l_run = xhalf_add(l_run);  // the two half-waves' key shares of each row
   float inv_l = (l_run > 0.f) ? 1.f / l_run : 0.f;
   float lse_l2 = (l_run > 0.f) ? m_run + __log2f(l_run) : -INFINITY;  // log2 units
   if (SCORE && a.sink_logit) {
