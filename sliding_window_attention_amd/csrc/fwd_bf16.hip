@@ -1164,37 +1164,65 @@ __global__ __launch_bounds__(256) void global_combine_kernel(const FwdArgs a, co
   constexpr int PS = D + 4;      // floats per record
   constexpr int LPR = D / 4;     // lanes per record
   constexpr int RPP = 256 / LPR; // records per pass
-  __shared__ float s_m[4];
+  __shared__ float s_m[RPP];
   __shared__ float s_l[RPP];
   __shared__ float4 s_o[RPP][LPR];
   const int u = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int c = tid % LPR, j = tid / LPR;
   const int nb = class_tiles(a.T, a.dil[h], kRowsPerWave);
   const float *ws = a.gws + (((long long)b * a.Hq + h) * a.G + u) * a.gnb * PS;
-  float mloc = -INFINITY;
-  for (int k = tid; k < nb; k += 256) mloc = fmaxf(mloc, ws[(long long)k * PS + D]);
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, x));
-  if (lane == 0) s_m[wave] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  float L = 0.f;
+  // One pass: thread (j, c) merges records j, j + RPP, ... (float4 c of each)
+  // against the largest of their maxima, then the RPP partial states merge in
+  // LDS against the overall maximum.  Every record load is independent.
+  constexpr int KMAX = 8;  // records per thread held at once
+  float mj = -INFINITY, L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int k = j; k < nb; k += RPP) {
-    const float *rec = ws + (long long)k * PS;
-    const float2 ml = *reinterpret_cast<const float2 *>(rec + D);
-    const float4 x = *reinterpret_cast<const float4 *>(rec + 4 * c);
-    const float sc = __builtin_amdgcn_exp2f(ml.x - M);
-    L = fmaf(sc, ml.y, L);
-    o.x = fmaf(sc, x.x, o.x);
-    o.y = fmaf(sc, x.y, o.y);
-    o.z = fmaf(sc, x.z, o.z);
-    o.w = fmaf(sc, x.w, o.w);
+  for (int k0 = j; k0 < nb; k0 += KMAX * RPP) {
+    float2 ml[KMAX];
+    float4 x[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      const int k = min(k0 + i * RPP, nb - 1);  // past the end: a repeat, weight 0
+      const float *rec = ws + (long long)k * PS;
+      ml[i] = *reinterpret_cast<const float2 *>(rec + D);
+      x[i] = *reinterpret_cast<const float4 *>(rec + 4 * c);
+    }
+    float mn = mj;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (k0 + i * RPP < nb) mn = fmaxf(mn, ml[i].x);
+    if (mn > -INFINITY) {
+      const float r = mj > -INFINITY ? __builtin_amdgcn_exp2f(mj - mn) : 0.f;
+      L *= r;
+      o.x *= r;
+      o.y *= r;
+      o.z *= r;
+      o.w *= r;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        const float sc = (k0 + i * RPP < nb && ml[i].x > -INFINITY) ? __builtin_amdgcn_exp2f(ml[i].x - mn) : 0.f;
+        L = fmaf(sc, ml[i].y, L);
+        o.x = fmaf(sc, x[i].x, o.x);
+        o.y = fmaf(sc, x[i].y, o.y);
+        o.z = fmaf(sc, x[i].z, o.z);
+        o.w = fmaf(sc, x[i].w, o.w);
+      }
+      mj = mn;
+    }
   }
+  if (c == 0) s_m[j] = mj;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < RPP; ++i) M = fmaxf(M, s_m[i]);
+  const float sj = mj > -INFINITY ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+  o.x *= sj;
+  o.y *= sj;
+  o.z *= sj;
+  o.w *= sj;
   s_o[j][c] = o;
-  if (c == 0) s_l[j] = L;
+  if (c == 0) s_l[j] = L * sj;
   __syncthreads();
   if (tid < D) {
     float Lt = 0.f, ot = 0.f;
