@@ -495,7 +495,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // (batch, head or head group, residue class, query tile); in a dilated
     // causal head group the waves take P heads x NW/P row blocks as above
     const int nblk = a.B * a.tiles_per_batch;
-    const int lid = xcd_remap(blockIdx.x, nblk);
+    // Dilated causal heads differ in work (shorter classes put more rows in
+    // the ramp), so whole head groups per XCD (the remap) would leave some
+    // XCDs idle early.  The dispatch order deals ids round-robin over the
+    // XCDs instead: ids 8 apart are tiles 8*BM class rows apart, whose bands
+    // (W keys) still overlap almost entirely in that XCD's L2.
+    const int lid = CDIL ? (int)blockIdx.x : xcd_remap(blockIdx.x, nblk);
     b = lid / a.tiles_per_batch;
     const int rem = lid % a.tiles_per_batch;
     // find the head (group): head_off[g] <= rem < head_off[g+1]
@@ -513,6 +518,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     int tile;
     class_tile_decode(a.T, dil, a.BM, rem - a.head_off[lo], &rho, &tile);
     n_cls = class_len(class_split(a.T, dil), rho);
+    if constexpr (CDIL) tile = ceil_div(n_cls, a.BM) - 1 - tile;  // heavy (full-band) tiles first
     tile_row0 = tile * a.BM;
     if constexpr (SYM) {
       h = lo;
