@@ -290,7 +290,7 @@ __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
 //
 // gp_load issues the loads after the banded loop and the out-of-band keys,
 // before the epilogue (K in the operand layout, the block's V rows, and for
-// d_h = 64 the first 32 global queries), so that they arrive while the
+// d_h = 64 the first 16 global queries), so that they arrive while the
 // epilogue runs; gp_finish stages V through the
 // wave's output slice (drained by the wave's output stores; LDS operations of
 // one wave run in order) for the transposing reads and does the rest.  Rows
@@ -300,38 +300,44 @@ __device__ inline bf16x8 tr_read8(const char *p0, const char *p1) {
 // unconditional.
 template <int D>
 struct GlobalPart {
-  static constexpr int KS = D / 16;  // k-steps of S (16-byte operand loads per lane)
+  // v_mfma_f32_16x16x32_bf16 tiles: 16 global rows per pass, two 16-key halves
+  static constexpr int KS = D / 32;  // k-steps of S (32 d per step)
   static constexpr int NV = D / 16;  // 16-byte chunks of the 32 V rows per lane
   static constexpr bool EARLY_Q = D == 64;  // registers allow the queries too
-  bf16x8 kf[KS];
+  bf16x8 kf[2][KS];  // K rows (A operand): [key half][k-step]
   u32x4 vr[NV];
-  bf16x8 qf[KS];
+  bf16x8 qf[KS];     // global queries (B operand)
 };
 
+// 16x16x32 operand layouts: lane l holds A[l % 16][8 (l / 16) + e] and
+// B[8 (l / 16) + e][l % 16] (e < 8); the result D[4 (l / 16) + i][l % 16] (i < 4).
 template <int D, bool GPROJ>
 __device__ inline void gp_load_q(bf16x8 *qf, const FwdArgs &a, int b, int h, int pos) {
   const uint16_t *qsrc = static_cast<const uint16_t *>(GPROJ ? a.qg : a.q);
   const uint16_t *qr = qsrc + (long long)b * a.q_sb + (long long)pos * a.q_st + (long long)h * D;
-  const int lh = (threadIdx.x & 63) >> 5;
+  const int q4 = (threadIdx.x & 63) >> 4;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const U4 *>(qr + ks * 16 + lh * 8));
+  for (int ks = 0; ks < D / 32; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const U4 *>(qr + ks * 32 + q4 * 8));
 }
 
 template <int D, bool GPROJ>
 __device__ inline void gp_load(GlobalPart<D> &g, const FwdArgs &a, const GlobalList &gl, int b, int h,
                                int kvh, int rho, int dil, int n_cls, int row0) {
-  const int lane = threadIdx.x & 63, lq = lane & 31, lh = lane >> 5;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4;
   // the first global positions before the K, V loads, so that the query
   // loads wait for this load only
-  const int pos0 = lq < a.G ? gl.idx[b * a.G + lq] : 0;
+  const int pos0 = l16 < a.G ? gl.idx[b * a.G + l16] : 0;
   const uint16_t *ksrc = static_cast<const uint16_t *>(GPROJ ? a.kg : a.k);
   const uint16_t *vsrc = static_cast<const uint16_t *>(GPROJ ? a.vg : a.v);
   const long long kv_off = (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   const int last = n_cls - 1;
-  const uint16_t *kr = ksrc + kv_off + (rho + (long long)dil * min(row0 + lq, last)) * a.k_st;
 #pragma unroll
-  for (int ks = 0; ks < GlobalPart<D>::KS; ++ks)
-    g.kf[ks] = as_bf16x8(*reinterpret_cast<const U4 *>(kr + ks * 16 + lh * 8));
+  for (int mb = 0; mb < 2; ++mb) {
+    const uint16_t *kr = ksrc + kv_off + (rho + (long long)dil * min(row0 + mb * 16 + l16, last)) * a.k_st;
+#pragma unroll
+    for (int ks = 0; ks < GlobalPart<D>::KS; ++ks)
+      g.kf[mb][ks] = as_bf16x8(*reinterpret_cast<const U4 *>(kr + ks * 32 + q4 * 8));
+  }
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int i = 0; i < GlobalPart<D>::NV; ++i) {
@@ -341,12 +347,23 @@ __device__ inline void gp_load(GlobalPart<D> &g, const FwdArgs &a, const GlobalL
   if constexpr (GlobalPart<D>::EARLY_Q) gp_load_q<D, GPROJ>(g.qf, a, b, h, pos0);
 }
 
+// Sum / max of x over the four lanes l % 16 + 16 j (v_permlane16_swap, then
+// v_permlane32_swap).
+__device__ inline float quad16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ inline float quad16_add(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xhalf_add(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
 template <int D, bool GPROJ>
 __device__ inline void gp_finish(GlobalPart<D> &g, const FwdArgs &a, const GlobalList &gl, char *vsl,
                                  int b, int h, int rho, int dil, int n_cls, int row0) {
   using Gm = Geo<D>;
-  constexpr int DB = D / 32, CPR = D / 8;
-  const int lane = threadIdx.x & 63, lq = lane & 31, lh = lane >> 5;
+  constexpr int DB = D / 16, CPR = D / 8;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
   for (int i = 0; i < GlobalPart<D>::NV; ++i) {
     const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
@@ -354,67 +371,68 @@ __device__ inline void gp_finish(GlobalPart<D> &g, const FwdArgs &a, const Globa
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-  // V^T operand offsets, as in the banded loop
+  // V^T operand: lane l takes d = 16 db + l % 16 at keys 4q .. 4q+3 (transposing
+  // read of a 4-row x 16-column block per 16 lanes) and 16 + 4q .. 16 + 4q+3
+  // (second read, 16 rows on), the key order of its P below
   uint32_t vop[DB];
   {
-    const int grp = lane >> 4, sl = lane & 15;
-    const int hh = grp >> 1, dg = grp & 1;
-    const int row = 4 * hh + (sl >> 2);
+    const int row = 4 * q4 + (l16 >> 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int c = 4 * db + 2 * dg + ((sl >> 1) & 1);
-      vop[db] = row * Gm::ROWB + ((c ^ swz_v<D>(row)) * 16) + 8 * (sl & 1);
+      const int c = 2 * db + ((l16 >> 1) & 1);
+      vop[db] = row * Gm::ROWB + ((c ^ swz_v<D>(row)) * 16) + 8 * (l16 & 1);
     }
   }
   const int last = n_cls - 1;
   const int blk = class_tile_base(a.T, dil, kRowsPerWave, rho) + row0 / kRowsPerWave;
-  for (int u0 = 0; u0 < a.G; u0 += 32) {
-    const int u = u0 + lq;
+  for (int u0 = 0; u0 < a.G; u0 += 16) {
+    const int u = u0 + l16;
     if (!GlobalPart<D>::EARLY_Q || u0 > 0) gp_load_q<D, GPROJ>(g.qf, a, b, h, u < a.G ? gl.idx[b * a.G + u] : 0);
-    f32x16 sg = f32x16{};
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 sg[2];
 #pragma unroll
-    for (int ks = 0; ks < GlobalPart<D>::KS; ++ks)
-      sg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g.kf[ks], g.qf[ks], sg, 0, 0, 0);
-    // element e holds key row0 + 8(e/4) + 4lh + e%4 for global row u
+    for (int mb = 0; mb < 2; ++mb) {
+      sg[mb] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < GlobalPart<D>::KS; ++ks)
+        sg[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.kf[mb][ks], g.qf[ks], sg[mb], 0, 0, 0);
+    }
+    // element (mb, i) holds key row0 + 16 mb + 4q + i for global row u
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (row0 + 8 * (e >> 2) + 4 * lh + (e & 3) > last) sg[e] = -INFINITY;
-      mx = fmaxf(mx, sg[e]);
-    }
-    const float mg = xhalf_max(mx) * a.sl2;  // finite: key row0 exists
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (row0 + 16 * mb + 4 * q4 + i > last) sg[mb][i] = -INFINITY;
+        mx = fmaxf(mx, sg[mb][i]);
+      }
+    const float mg = quad16_max(mx) * a.sl2;  // finite: key row0 exists
     float rs = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sg[e] = __builtin_amdgcn_exp2f(fmaf(sg[e], a.sl2, -mg));
-      rs += sg[e];
-    }
-    const float lg = xhalf_add(rs);
-    f32x16 og[DB];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) og[db] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      U4 pw;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pw.w[w] = pack_bf16(sg[8 * kk + 2 * w], sg[8 * kk + 2 * w + 1]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const char *p0 = vsl + kk * 16 * Gm::ROWB + vop[db];
-        og[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read8(p0, p0 + 8 * Gm::ROWB), as_bf16x8(pw),
-                                                         og[db], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        sg[mb][i] = __builtin_amdgcn_exp2f(fmaf(sg[mb][i], a.sl2, -mg));
+        rs += sg[mb][i];
       }
-    }
-    if (u < a.G) {
-      float *dst = a.gws + ((((long long)b * a.Hq + h) * a.G + u) * a.gnb + blk) * (D + 4);
+    const float lg = quad16_add(rs);
+    U4 pw;
+    pw.w[0] = pack_bf16(sg[0][0], sg[0][1]);
+    pw.w[1] = pack_bf16(sg[0][2], sg[0][3]);
+    pw.w[2] = pack_bf16(sg[1][0], sg[1][1]);
+    pw.w[3] = pack_bf16(sg[1][2], sg[1][3]);
+    // every lane takes part in the reads and products (each output column
+    // needs the operand rows of all lanes); only global rows that exist store
+    float *dst = a.gws + ((((long long)b * a.Hq + h) * a.G + min(u, a.G - 1)) * a.gnb + blk) * (D + 4);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<float4 *>(dst + db * 32 + 8 * g4 + 4 * lh) =
-              make_float4(og[db][4 * g4], og[db][4 * g4 + 1], og[db][4 * g4 + 2], og[db][4 * g4 + 3]);
-      if (lh == 0) *reinterpret_cast<float2 *>(dst + D) = make_float2(mg, lg);
+    for (int db = 0; db < DB; ++db) {
+      const char *p0 = vsl + vop[db];
+      const f32x4 og = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_read8(p0, p0 + 16 * Gm::ROWB),
+                                                               as_bf16x8(pw), f32x4{}, 0, 0, 0);
+      if (u < a.G)
+        *reinterpret_cast<float4 *>(dst + db * 16 + 4 * q4) = make_float4(og[0], og[1], og[2], og[3]);
     }
+    if (u < a.G && q4 == 0) *reinterpret_cast<float2 *>(dst + D) = make_float2(mg, lg);
   }
 }
 
