@@ -26,6 +26,10 @@ SMALL = [
     (2, 520, 4, 64, 64, [1, 1, 2, 2], [[0, 8], [200, 519]]),
     (1, 129, 2, 128, 63, [4, 1], [[3, 64, 65, 100]]),
     (1, 90, 2, 64, 5, [100, 1], [[0]]),
+    # 16 < G <= 32: two 16-row passes of the global-row block states, global
+    # keys added after the band
+    (1, 300, 2, 64, 9, [1, 3], [list(range(0, 300, 12))]),
+    (1, 200, 2, 128, 30, [2, 1], [list(range(1, 200, 7))]),
     # more than 32 global tokens: the tile-of-global-keys path with shared projections
     (1, 300, 2, 64, 9, [1, 3], [list(range(0, 300, 7))]),
     (2, 260, 2, 128, 20, [2, 1], [list(range(3, 260, 6)), list(range(0, 43))]),
@@ -71,7 +75,8 @@ def _class_blocks(T, dil, n=32):
     (2, 300, 4, 64, 20, [1, 2, 3, 1], [[0, 77], [5, 299]]),
     (1, 129, 2, 128, 63, [4, 1], [[3, 64, 65, 100]]),
     (1, 300, 2, 64, 9, [1, 3], [list(range(0, 300, 7))]),
-], ids=["d64", "d128", "43globals"])
+    (1, 200, 2, 128, 30, [2, 1], [list(range(1, 200, 7))]),
+], ids=["d64", "d128", "43globals", "29globals_d128"])
 def test_longformer_global_rows_both_paths(case):
     B, T, H, D, r, dil, gl = case
     c = inp.LongformerCase(B=B, T=T, H=H, D=D, r=r, dilation=dil, globals_=gl[0], dtype="bf16",
