@@ -272,9 +272,12 @@ swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *
  * only the first cap are written), or -1 on invalid arguments.  Host only. */
 int swa_band_tiles(int mode, int T, int w_or_r, int BM, int BN, int32_t *out, int cap);
 
-/* Writes the device-side window predicate the kernels use as a uint8 [T, T]
- * matrix (1 = attended) into mask_dev (device).  Causal: W = w_or_r.
- * Symmetric: r = w_or_r, dilation dil, HOST global list global_idx[G]. */
+/* Writes the connectivity sets as a uint8 [T, T] matrix (1 = attended) into
+ * mask_dev (device), evaluated on the GPU from the per-row key bounds and the
+ * residue-class mapping the banded kernels mask with (the same inline code).
+ * It does not run the kernels' tile-level masking; that is read out through
+ * the kernels themselves.  Causal: W = w_or_r.  Symmetric: r = w_or_r,
+ * dilation dil, HOST global list global_idx[G]. */
 swa_status swa_debug_index_mask(int mode, int T, int w_or_r, int dil, const int32_t *global_idx,
                                 int G, uint8_t *mask_dev, void *stream);
 

@@ -133,7 +133,7 @@ def swa_decode(q, k_cache, v_cache, slot_pos, cur_pos, W, scale=None):
 
 
 def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None, n_sink=0,
-                       sink_logit=None):
+                       sink_logit=None, rows=None):
     """A chunk of L query tokens per request over a ring cache of S slots.
 
     [G3] "How it works": queries carry absolute positions ([B, L]) and the cache
@@ -143,22 +143,25 @@ def swa_prefill_cached(q, k_cache, v_cache, slot_pos, q_pos, W, scale=None, n_si
     single-token chunk is ring decode.  ``n_sink`` / ``sink_logit`` as in
     ``swa_prefill`` (slots holding one of the first n_sink positions stay visible).
     q: [B, L, H_q, d_h]; k_cache, v_cache: [B, H_kv, S, d_h]; slot_pos: [B, S]
-    (< 0 = empty); q_pos: [B, L].  Returns o [B, L, H_q, d_h], lse [B, H_q, L].
+    (< 0 = empty); q_pos: [B, L].  ``rows`` optionally restricts the computation
+    to those query tokens.  Returns o [B, R, H_q, d_h], lse [B, H_q, R]
+    (R = len(rows) or L).
     """
     B, L, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     group = Hq // Hkv
     sc = _default_scale(D, scale)
-    o = np.zeros((B, L, Hq, v_cache.shape[-1]), dtype=np.float64)
-    lse = np.zeros((B, Hq, L), dtype=np.float64)
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((B, len(rows), Hq, v_cache.shape[-1]), dtype=np.float64)
+    lse = np.zeros((B, Hq, len(rows)), dtype=np.float64)
     for b in range(B):
-        for t in range(L):
+        for ri, t in enumerate(rows):
             S_t = decode_index_set(slot_pos[b], int(q_pos[b, t]), W, n_sink)
             for h in range(Hq):
                 kvh = h // group
                 z = None if sink_logit is None else sink_logit[h]
-                o[b, t, h], lse[b, h, t] = attend(q[b, t, h], k_cache[b, kvh, S_t],
-                                                  v_cache[b, kvh, S_t], sc, z)
+                o[b, ri, h], lse[b, h, ri] = attend(q[b, t, h], k_cache[b, kvh, S_t],
+                                                    v_cache[b, kvh, S_t], sc, z)
     return o, lse
 
 

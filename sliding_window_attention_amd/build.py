@@ -6,6 +6,7 @@ Usage: ``python -m sliding_window_attention_amd.build``.  Always recompiles.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -47,12 +48,15 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     inc = ["-I", os.path.join(HERE, "..", "include")]
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         extra = ["-fno-honor-nans", "-mno-amdgpu-ieee"] if src in RELAXED_NAN else []
-        _run([HIPCC] + FLAGS + extra + inc + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        cmds.append([HIPCC] + FLAGS + extra + inc + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # one hipcc per source, side by side
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)

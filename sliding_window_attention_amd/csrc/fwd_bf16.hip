@@ -407,20 +407,21 @@ __device__ inline void gp_finish(GlobalPart<D> &g, const FwdArgs &a, const Globa
         mx = fmaxf(mx, sg[mb][i]);
       }
     const float mg = quad16_max(mx) * a.sl2;  // finite: key row0 exists
-    float rs = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sg[mb][i] = __builtin_amdgcn_exp2f(fmaf(sg[mb][i], a.sl2, -mg));
-        rs += sg[mb][i];
-      }
-    const float lg = quad16_add(rs);
+      for (int i = 0; i < 4; ++i) sg[mb][i] = __builtin_amdgcn_exp2f(fmaf(sg[mb][i], a.sl2, -mg));
     U4 pw;
     pw.w[0] = pack_bf16(sg[0][0], sg[0][1]);
     pw.w[1] = pack_bf16(sg[0][2], sg[0][3]);
     pw.w[2] = pack_bf16(sg[1][0], sg[1][1]);
     pw.w[3] = pack_bf16(sg[1][2], sg[1][3]);
+    // row sum over the rounded weights the product uses (v_dot2 against ones)
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float rs = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w[w]), ones, rs, false);
+    const float lg = quad16_add(rs);
     // every lane takes part in the reads and products (each output column
     // needs the operand rows of all lanes); only global rows that exist store
     float *dst = a.gws + ((((long long)b * a.Hq + h) * a.G + min(u, a.G - 1)) * a.gnb + blk) * (D + 4);
@@ -917,11 +918,31 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
         }
       }
   };
+  // Ring mode: value rows of the slots of a staged tile that hold no token
+  // (negative position, or past the ring's end) are zeroed in LDS before any
+  // wave reads the tile.  Their weights are 0 already, but 0 times the NaN or
+  // Inf bits an unwritten slot may hold would not be.  Every wave sees the
+  // same slot positions, so all take the same branch and the same barrier.
+  auto ring_zero_holes = [&](char *stg, int j) {
+    const int n_in = min(BN, a.S - (tr.lo + j) * BN);
+    const int sp = reinterpret_cast<const int *>(stg + SP_OFF)[lane % BN];
+    const uint64_t hole = __builtin_amdgcn_ballot_w64((lane % BN) >= n_in || sp < 0);
+    if (hole == 0) return;
+    constexpr int CPR = D / 8, RPW = 64 / CPR;  // 16-byte chunks per row, rows per store
+    char *vt = stg + Gm::TILE_B;
+#pragma unroll
+    for (int r0 = wave * RPW; r0 < BN; r0 += NW * RPW) {
+      const int row = r0 + lane / CPR;
+      if ((hole >> row) & 1ull)
+        *reinterpret_cast<u32x4 *>(vt + row * Gm::ROWB + (lane % CPR) * 16) = u32x4{0, 0, 0, 0};
+    }
+    lds_barrier();
+  };
   // Attended keys of row my_row inside the window, [lo_key, hi_key]: the
   // causal predicate (t-W < s <= t) or the symmetric one (|i-j| <= r), cut at
   // the class length.
-  const int lo_key = SYM ? my_row - a.W : my_row - a.W + 1;
-  const int hi_key = min(SYM ? my_row + a.W : my_row, n_cls - 1);
+  int lo_key, hi_key;
+  row_key_bounds(SYM, my_row, a.W, n_cls, &lo_key, &hi_key);
   // mask of a partial tile: the window predicate (global positions left out
   // when gcols marks some), or for a tile of global keys the existing globals
   auto mask = [&](int j, f32x16 *sv, uint64_t gcols) {
@@ -993,9 +1014,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     const int kj = tr.lo + j;
     // a wave computes the tiles of its rows' band, the extra tiles, and key
     // tile 0 when sink tokens live there
-    const char *ks = smem + st * STAGE_B;
+    char *ks = smem + st * STAGE_B;
     int rc = 1;  // ring mode: tile class (0 = nothing attended, skip)
-    if constexpr (RING) rc = has_rows ? ring_class(ks, j) : 0;
+    if constexpr (RING) {
+      ring_zero_holes(ks, j);
+      rc = has_rows ? ring_class(ks, j) : 0;
+    }
     if (has_rows && rc != 0 &&
         (j >= n_win || (kj >= wr.lo && kj <= wr.hi))) {
       f32x16 sv[KB];

@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void split_kernel(const SplitArgs a, const Glo
   __shared__ float sc[kMaxQ][kMaxChunk];
   __shared__ float red[4][kMaxQ][D];
   __shared__ float ml[kMaxQ][2];
+  __shared__ uint8_t key_ok[kMaxChunk];  // key r of the chunk is attended
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(256) void split_kernel(const SplitArgs a, const Glo
         valid = p >= 0 && p > cur - a.W && p <= cur;
       }
     }
+    if (sub == 0 && r < n) key_ok[r] = valid;
     for (int qi = 0; qi < nq; ++qi) {
       float part = 0.f;
 #pragma unroll
@@ -141,9 +143,11 @@ __global__ __launch_bounds__(256) void split_kernel(const SplitArgs a, const Glo
   for (int qi = 0; qi < kMaxQ; ++qi)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
+  // keys outside the set are skipped, not multiplied by a zero weight: the
+  // value rows of empty or stale ring slots may hold any bits
   for (int r0 = 0; r0 < n; r0 += RPR) {
     const int r = r0 + grp;
-    if (r < n) {
+    if (r < n && key_ok[r]) {
       float vx[8];
       load8<F32>(vb + ((c0 + r) * a.k_sr + sub * 8) * ES, vx);
 #pragma unroll
@@ -441,16 +445,25 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
     const float m_new = fmaxf(m_run, mx * a.sl2);
     const float mu = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], a.sl2, -mu));
+    // P -> bf16 (RNE), rows paired as (key, key + 8): both live in this lane
+    // as elements j and j + 4.  The row sum is taken over these rounded
+    // weights (v_dot2 against ones, fp32), the ones the product uses.
+    uint32_t pk[8];
     float rs = 0.f;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], a.sl2, -mu));
-      rs += s[j];
+      if ((j & 4) == 0) {
+        const int u = (j >> 3) * 4 + (j & 3);
+        pk[u] = pack2_bf16(s[j], s[j + 4]);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[u]), ones, rs, false);
+      }
     }
     l_run = fmaf(l_run, alpha, xhalf_add(rs));
     m_run = m_new;
-    // P pairs -> LDS.  Rows paired as (key, key + 8): both live in this lane
-    // as elements j and j + 4.
+    // P pairs -> LDS
     if (lq < QG) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -463,7 +476,7 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
             pi = j >> 3;
             rg = 4 * lh + (j & 3);
           }
-          ppair[parity][pi][rg][lq] = pack2_bf16(s[j], s[j + 4]);
+          ppair[parity][pi][rg][lq] = pk[(j >> 3) * 4 + (j & 3)];
         }
       }
     }
@@ -493,10 +506,15 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
         i0 = 2 * pi;
         i1 = i0 + 1;
       }
+      // value rows of keys outside the set (empty, stale or future slots, or
+      // past the end) are zeroed: their weight is 0, but 0 times the NaN or
+      // Inf bits an unwritten slot may hold would not be
+      const uint32_t z0 = ((vm >> (RG * i0 + g)) & 1ull) ? 0xffffffffu : 0u;
+      const uint32_t z1 = ((vm >> (RG * i1 + g)) & 1ull) ? 0xffffffffu : 0u;
       uint32_t w[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t x0 = blk.v[i0].w[e], x1 = blk.v[i1].w[e];
+        const uint32_t x0 = blk.v[i0].w[e] & z0, x1 = blk.v[i1].w[e] & z1;
         w[2 * e] = (x0 & 0xffffu) | (x1 << 16);
         w[2 * e + 1] = (x0 >> 16) | (x1 & 0xffff0000u);
       }
@@ -660,16 +678,24 @@ __global__ void debug_mask_kernel(int mode, int T, int w_or_r, int dil, const Gl
   const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
   if (i >= (long long)T * T) return;
   const int t = (int)(i / T), s = (int)(i % T);
+  // the row's key bounds of the banded kernels (row_key_bounds), in the
+  // residue-class index space they run in
   bool on;
+  int lo, hi;
   if (mode == SWA_MODE_CAUSAL) {
-    on = causal_in(t, s, w_or_r);
+    row_key_bounds(false, t, w_or_r, T, &lo, &hi);
+    on = s >= lo && s <= hi;
   } else {
     bool t_glob = false, s_glob = false;
     for (int g = 0; g < G; ++g) {
       t_glob |= gl.idx[g] == t;
       s_glob |= gl.idx[g] == s;
     }
-    on = t_glob || s_glob || dilated_in(t, s, w_or_r, dil);
+    const int rho = t % dil;
+    const int n_cls = class_len(class_split(T, dil), rho);
+    row_key_bounds(true, t / dil, w_or_r, n_cls, &lo, &hi);
+    const bool win = s % dil == rho && s / dil >= lo && s / dil <= hi;
+    on = t_glob || s_glob || win;
   }
   mask[i] = on ? 1 : 0;
 }

@@ -1,8 +1,10 @@
 // swa_internal.h — definitions shared by the host launchers and the gfx950 kernels.
 //
-// The window predicates and the band-tile schedule are written once here as
-// __host__ __device__ functions: the kernels run them, and swa_band_tiles /
-// swa_debug_index_mask export exactly the same code for testing.
+// The row key bounds and the band-tile schedule are written once here as
+// __host__ __device__ functions: the banded kernels run them, swa_band_tiles
+// exports the schedule and swa_debug_index_mask evaluates the bounds for
+// testing.  (The kernels' tile-level mask arithmetic on top of the bounds is
+// read out through the kernels themselves by the tests.)
 //
 // Page tags used in comments:
 //   [KB] "Sliding Window Attention", LLM architecture knowledge base (lizeman.github.io)
@@ -35,6 +37,20 @@ __host__ __device__ inline bool dilated_in(int i, int j, int r, int dil) {
   if (d % dil != 0) return false;
   const int k = d / dil;
   return k <= r && -k <= r;
+}
+
+// Attended keys of one row as an interval in the banded kernels' index space:
+// causal row t of a sequence of n keys attends [t-W+1, min(t, n-1)] ([KB] §2
+// N_t, cut at 0 by the key range); row i of one residue class of length n
+// attends [i-r, min(i+r, n-1)] ([PP] §1.1 inside the class, §3.1).  The banded
+// kernel masks its partial tiles by comparing key indices with these bounds;
+// swa_debug_index_mask evaluates the same bounds (and the same class mapping)
+// for every (row, key) pair.
+__host__ __device__ inline void row_key_bounds(bool symmetric, int i, int w_or_r, int n, int *lo,
+                                               int *hi) {
+  *lo = symmetric ? i - w_or_r : i - w_or_r + 1;
+  const int h = symmetric ? i + w_or_r : i;
+  *hi = h < n - 1 ? h : n - 1;
 }
 
 // ---------------------------------------------------------------- band tiles

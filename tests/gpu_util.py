@@ -11,6 +11,13 @@ TOL_BF16 = 2e-2
 TOL_F32 = 1e-5
 TOL_LSE_BF16 = 2e-3   # lse sees exact bf16 products summed in fp32
 TOL_LSE_F32 = 1e-5
+# lse when q = 0: every score is 0, every weight is exactly 1 (2^0, also in
+# bf16), so the row sum l is the integer |S_t| held exactly in fp32 (< 2^24)
+# and lse = log2(l) ln 2 carries only the rounding of the hardware log2 (about
+# one ulp) and of the product: |error| <= 2^-22 |lse| < 3e-6 for |S_t| <= 2^15.
+# A one-key change of |S_t| moves lse by ln((n+1)/n) >= 1/(n+1), i.e. by at
+# least 3e-5 for n <= 32768, so this bound separates |S_t| from |S_t| +- 1.
+TOL_LSE_EXACT = 1e-5
 
 
 def banner(msg):

@@ -138,3 +138,28 @@ def test_cached_full_size_sampled_rows():
     b_idx = rng.integers(0, c.B, size=48)
     t_idx = np.concatenate([[0, c.L - 1, 1, c.L - 2], rng.integers(0, c.L, size=44)])
     _compare(q, kc, vc, sp, qp, c.W, "bf16", rows=(b_idx, t_idx))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,S,W,Hq,Hkv,D,p_lo,p_hi", [
+    (2, 48, 64, 40, 4, 2, 128, 0, 10),        # ring not yet full
+    (2, 37, 100, 64, 8, 2, 128, 64, 300),
+    (3, 20, 130, 64, 4, 1, 64, 30, 60),       # ragged last slot tile
+])
+def test_cached_ignores_nonfinite_bits_of_empty_slots(dtype, B, L, S, W, Hq, Hkv, D, p_lo, p_hi):
+    # Slots that hold no token (negative position) may contain any bits, e.g.
+    # a cache from torch.empty: they must not reach the output.
+    c = inp.ChunkCase(B=B, L=L, S=S, W=W, Hq=Hq, Hkv=Hkv, D=D, p_lo=p_lo, p_hi=p_hi, dtype=dtype,
+                      seed=B * 7 + L + S)
+    q, kc, vc, sp, qp = inp.chunk_inputs(c)
+    spn = sp.numpy().copy()
+    rng = np.random.default_rng(L + S)
+    kn, vn = kc.clone(), vc.clone()
+    for b in range(B):
+        spn[b, rng.choice(S, size=5, replace=False)] = -1
+        empty = np.nonzero(spn[b] < 0)[0]
+        for i, j in enumerate(empty):
+            fill = [float("nan"), float("inf"), float("-inf")][i % 3]
+            kn[b, :, j] = fill
+            vn[b, :, j] = fill
+    _compare(q, kn, vn, torch.from_numpy(spn), qp, W, dtype)

@@ -126,3 +126,30 @@ def test_cache_write_then_decode(dtype):
     assert np.array_equal(sp.cpu().numpy(), osp)
     q = torch.from_numpy(inp.normal((B, Hq, D), 17)).to(tdt)
     _compare(q, kc.cpu(), vc.cpu(), sp.cpu(), torch.full((B,), T - 1, dtype=torch.int32), W, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,W,Hq,Hkv,D", [(4, 200, 8, 2, 128), (64, 512, 32, 8, 128),
+                                          (3, 96, 4, 4, 64)])
+def test_decode_ignores_nonfinite_bits_of_unattended_slots(dtype, B, W, Hq, Hkv, D):
+    # Empty, stale and future slots are outside the window: whatever bits they
+    # hold (NaN, Inf) must not reach the output ([KB] §2 "KV cache": only the
+    # positions of the window are attended).
+    c = inp.DecodeCase(B=B, W=W, Hq=Hq, Hkv=Hkv, D=D, cur_lo=0, cur_hi=3 * W, dtype=dtype,
+                       seed=B + W + D)
+    q, kc, vc, sp, cur = inp.decode_inputs(c)
+    spn = sp.numpy().copy()
+    curn = cur.numpy().astype(np.int64)
+    rng = np.random.default_rng(B * W)
+    kn, vn = kc.clone(), vc.clone()
+    for b in range(B):
+        js = rng.choice(W, size=9, replace=False)
+        spn[b, js[:3]] = -1                                    # empty
+        spn[b, js[3:6]] = curn[b] - W - rng.integers(0, 5, 3)  # stale
+        spn[b, js[6:]] = curn[b] + 1 + rng.integers(0, 5, 3)   # future
+        bad = np.nonzero((spn[b] < 0) | (spn[b] <= curn[b] - W) | (spn[b] > curn[b]))[0]
+        for i, j in enumerate(bad):
+            fill = [float("nan"), float("inf"), float("-inf")][i % 3]
+            kn[b, :, j] = fill
+            vn[b, :, j] = fill
+    _compare(q, kn, vn, torch.from_numpy(spn), cur, W, dtype)

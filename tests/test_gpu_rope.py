@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import pool
 from sliding_window_attention_amd import binding as bd
 from sliding_window_attention_amd import inputs as inp
 from gpu_util import TOL_BF16, TOL_F32, TOL_LSE_BF16, TOL_LSE_F32, banner, dev, host, max_err
@@ -125,18 +126,41 @@ def test_prefill_rope_f32(case):
     assert max_err(lse, rl) <= TOL_LSE_F32
 
 
-def test_prefill_rope_local_layer_fullsize_sampled():
+def test_prefill_rope_local_layer_fullsize_row_set():
     # the local-layer shape (B=2, T=32768, W=1024, H_q=32, H_kv=16) with the
-    # rotation done inside the call instead of by the input generator
+    # rotation done inside the call instead of by the input generator; rows
+    # [0, W+256), [T-256, T) and 4096 seeded random rows, all heads
     c = inp.PrefillCase(B=2, T=32768, Hq=32, Hkv=16, D=128, W=1024, seed=1002)
     q, k, v = inp.prefill_inputs(c)
     banner("prefill_rope local-layer full size")
     o, lse = bd.prefill_rope(dev(q), dev(k), dev(v), c.W, 1e4, return_lse=True)
     torch.cuda.synchronize()
+    o, lse = o.cpu(), host(lse)
     rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([np.arange(0, 24), np.arange(c.T - 24, c.T),
-                                     rng.integers(0, c.T, 24)]))
-    ro, rl = oracle.swa_prefill(inp.widen(q), inp.widen(k), inp.widen(v), c.W, rows=rows,
-                                rope_base=1e4)
-    assert max_err(host(o)[:, rows], ro) <= TOL_BF16
-    assert np.all(np.abs(host(lse)[:, :, rows] - rl) <= _lse_bound(q, k, c.W, 1e4, rows))
+    rows = np.unique(np.concatenate([np.arange(0, c.W + 256), np.arange(c.T - 256, c.T),
+                                     rng.integers(0, c.T, 4096)]))
+    # the oracle's rotation (fp64) of k at every position and of q at the
+    # compared rows, then the oracle's plain prefill over those rows: the same
+    # as oracle.swa_prefill(..., rope_base=1e4) on them
+    k_rot = oracle.rope_rotate_half(inp.widen(k), np.arange(c.T), 1e4)
+    q_rot = np.zeros(q.shape, dtype=np.float64)
+    q_rot[:, rows] = oracle.rope_rotate_half(inp.widen(q)[:, rows], rows, 1e4)
+    # lse bound of _lse_bound with sum_i |q_i k_i| <= |q| |k| (Cauchy-Schwarz)
+    # and the largest |k_s| of the row's window
+    qn = np.linalg.norm(q_rot[:, rows], axis=-1)                 # [B, R, Hq]
+    kn = np.linalg.norm(k_rot, axis=-1)                          # [B, T, Hkv]
+    pad = np.concatenate([np.zeros((c.B, c.W - 1, c.Hkv)), kn], axis=1)
+    kmax = np.lib.stride_tricks.sliding_window_view(pad, c.W, axis=1).max(axis=-1)  # [B, T, Hkv]
+    group = c.Hq // c.Hkv
+    bound = TOL_LSE_BF16 + (qn * np.repeat(kmax[:, rows], group, axis=2)).transpose(0, 2, 1) \
+        / np.sqrt(c.D) * (2.0 ** -8 + 2.0 ** -18)                # [B, Hq, R]
+    pos = {int(t): i for i, t in enumerate(rows)}
+    worst = 0.0
+    for rc, (ro, rl) in pool.run_rows(oracle.swa_prefill, (q_rot, k_rot, inp.widen(v)), rows,
+                                      dict(W=c.W)):
+        e = max_err(host(o[:, rc]), ro)
+        worst = max(worst, e)
+        assert e <= TOL_BF16, f"rows {rc[0]}..{rc[-1]} max err {e}"
+        ix = [pos[int(t)] for t in rc]
+        assert np.all(np.abs(lse[:, :, rc] - rl) <= bound[:, :, ix]), f"lse rows {rc[0]}..{rc[-1]}"
+    banner(f"prefill_rope local-layer: {len(rows)} rows x all heads, max err {worst:.3e}")
