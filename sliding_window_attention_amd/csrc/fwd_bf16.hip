@@ -49,6 +49,7 @@
 // (prathamp.com); [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai);
 // [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive.pages.dev).
 
+#include <algorithm>
 #include <climits>
 
 #include "swa_internal.h"
@@ -515,11 +516,17 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // causal head group the waves take P heads x NW/P row blocks as above
     const int nblk = a.B * a.tiles_per_batch;
     // Dilated causal heads differ in work (shorter classes put more rows in
-    // the ramp), so whole head groups per XCD (the remap) would leave some
-    // XCDs idle early.  The dispatch order deals ids round-robin over the
-    // XCDs instead: ids 8 apart are tiles 8*BM class rows apart, whose bands
-    // (W keys) still overlap almost entirely in that XCD's L2.
-    const int lid = CDIL ? (int)blockIdx.x : xcd_remap(blockIdx.x, nblk);
+    // the ramp), so the host cuts the enumeration into 8 ranges of equal work,
+    // one per XCD: each XCD runs consecutive tiles of few classes, whose bands
+    // share its L2.  Workgroups past their XCD's range exit at once.
+    int lid;
+    if constexpr (CDIL) {
+      const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+      lid = a.xcd_off[x] + i;
+      if (lid >= a.xcd_off[x + 1]) return;
+    } else {
+      lid = xcd_remap(blockIdx.x, nblk);
+    }
     b = lid / a.tiles_per_batch;
     const int rem = lid % a.tiles_per_batch;
     // find the head (group): head_off[g] <= rem < head_off[g+1]
@@ -1301,8 +1308,13 @@ hipError_t launch_global_combine(const FwdArgs &a, int D, const GlobalList *gl, 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *gl,
                            hipStream_t st) {
   const bool sym = mode == kSymmetric || mode == kSymmetricProj;
-  const int nblk = (sym || mode == kCausalDil) ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
+  int nblk = (sym || mode == kCausalDil) ? a.B * a.tiles_per_batch : a.B * a.n_hg * a.n_qt;
   if (nblk <= 0) return hipSuccess;
+  if (mode == kCausalDil) {  // 8 work-balanced XCD ranges
+    int most = 0;
+    for (int x = 0; x < 8; ++x) most = std::max(most, a.xcd_off[x + 1] - a.xcd_off[x]);
+    nblk = 8 * most;
+  }
   constexpr int NWC = SWA_FWD_WAVES;
   if (a.NW != fwd_waves(mode)) return hipErrorInvalidValue;
   dim3 grid(nblk), block(64 * a.NW);

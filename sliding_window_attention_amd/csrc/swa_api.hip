@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "swa_internal.h"
 
@@ -85,6 +86,40 @@ int lf_block_cap(int T) {
   int m = 0;
   for (int d = 1; d <= kBlockMaxDil; ++d) m = std::max(m, class_tiles(T, d, kRowsPerWave));
   return m;
+}
+
+// Dilated causal launch: cut the work items (batch, head group, class, query
+// tile; the kernel's enumeration, each class's tiles heaviest first) into 8
+// consecutive ranges of equal work, one per XCD.  Work of a tile = the key
+// tiles its band visits (causal_tile_range in class index space).
+void dilated_xcd_ranges(FwdArgs &a, int BN) {
+  std::vector<long long> pre(1, 0);  // prefix sums of work over one batch row
+  pre.reserve(a.tiles_per_batch + 1);
+  for (int g = 0; g < a.n_hg; ++g) {
+    const int dil = a.dil[g];
+    const ClassSplit cs = class_split(a.T, dil);
+    for (int rho = 0; rho < dil; ++rho) {
+      const int n_cls = class_len(cs, rho), nt = ceil_div(n_cls, a.BM);
+      for (int i = 0; i < nt; ++i) {
+        const int tile = nt - 1 - i;  // heavy first, as the kernel decodes it
+        const int t0 = tile * a.BM, t1 = std::min(t0 + a.BM, n_cls) - 1;
+        const TileRange tr = causal_tile_range(t0, t1, a.W, BN);
+        pre.push_back(pre.back() + (tr.hi - tr.lo + 1));
+      }
+    }
+  }
+  const long long per_b = pre.back(), total = per_b * a.B;
+  const long long n_items = (long long)a.B * a.tiles_per_batch;
+  a.xcd_off[0] = 0;
+  for (int x = 1; x < 8; ++x) {
+    // first item whose cumulative work reaches x/8 of the total
+    const long long target = (total * x + 7) / 8;
+    const long long b = target / per_b, rem = target % per_b;
+    const long long i = std::lower_bound(pre.begin(), pre.end(), rem) - pre.begin();
+    a.xcd_off[x] = (int)std::min(n_items, b * a.tiles_per_batch + i);
+  }
+  a.xcd_off[8] = (int)n_items;
+  for (int x = 1; x <= 8; ++x) a.xcd_off[x] = std::max(a.xcd_off[x], a.xcd_off[x - 1]);
 }
 
 }  // namespace
@@ -253,6 +288,7 @@ swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const
   // bf16 kernels address one batch slice of K/V with 32-bit byte offsets
   if (tiles * B > 0x7fffffffLL || a.k_sb * 2 >= (1LL << 31)) return SWA_ERR_UNSUPPORTED;
   a.tiles_per_batch = (int)tiles;
+  dilated_xcd_ranges(a, key_tile(d_h));
   return hip_status(launch_fwd_bf16(a, kCausalDil, d_h, &gl, st));
 }
 

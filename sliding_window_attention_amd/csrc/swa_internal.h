@@ -222,6 +222,10 @@ struct FwdArgs {
   // revolutions (rope_rev0 = 1 / 2pi, rope_step = base^(-2/D))
   int rope;
   double rope_rev0, rope_step;
+  // dilated causal mode: XCD x runs the work items [xcd_off[x], xcd_off[x+1])
+  // of the enumeration (ranges cut for equal work, see dilated_xcd_ranges);
+  // the grid is 8 * the longest range
+  int xcd_off[9];
 };
 
 constexpr int kMaxSinks = 32;  // few: the causal kernel adds them one key at a time
