@@ -35,9 +35,11 @@
  *     (contiguous groups; H_q must be a multiple of H_kv).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
  *     Every argument is validated on the host before any HIP call; on error
- *     nothing is launched.  The library keeps no pointer after returning,
- *     allocates no device memory, and has no mutable global state: concurrent
- *     calls from several host threads are safe.
+ *     nothing is launched.  The library keeps no pointer after returning and
+ *     allocates no device memory; its only global state is the per-GPU
+ *     scratch array of swa_decode_noalloc and that array's cached address.
+ *     Concurrent calls from several host threads are safe, except overlapping
+ *     swa_decode_noalloc calls on one GPU (see there).
  *   - Errors: SWA_ERR_INVALID (bad argument), SWA_ERR_UNSUPPORTED (valid but
  *     not implemented), SWA_ERR_WORKSPACE (workspace too small), SWA_ERR_HIP
  *     (a HIP launch failed; device faults surface at stream synchronisation).
@@ -158,6 +160,26 @@ swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const vo
                       const int32_t *slot_pos, const int32_t *cur_pos, void *o, float *lse,
                       int B, int W, int H_q, int H_kv, int d_h, float scale, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* swa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It allocates nothing: the split partial states go
+ * to a scratch array of SWA_DECODE_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory, one per GPU, for the life of the process (its
+ * address is looked up on the first call on a device; the calling thread's
+ * current device is used, and `stream` must belong to it).  Every call on a
+ * GPU shares that GPU's array and leaves its contents behind (nothing in it
+ * needs to start at zero): calls that overlap on one GPU (other streams,
+ * other threads) race on it; calls in one stream are ordered and safe.
+ * Arguments, results and errors are those of swa_decode, plus
+ * SWA_ERR_WORKSPACE when swa_decode_workspace_size() for the shape exceeds
+ * SWA_DECODE_NOALLOC_SCRATCH_BYTES (nothing is launched then) and SWA_ERR_HIP
+ * if the scratch address cannot be obtained. */
+#define SWA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+swa_status swa_decode_noalloc(swa_dtype dt, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *slot_pos,
+                              const int32_t *cur_pos, void *o, float *lse, int B, int W, int H_q,
+                              int H_kv, int d_h, float scale, void *stream);
 
 /* Ring-cache append: writes k_new[b], v_new[b] ([B, H_kv, d_h]) into slot
  * pos[b] mod W of k_cache/v_cache ([B, H_kv, W, d_h]) and sets

@@ -40,6 +40,7 @@ def lib():
         L.swa_decode_workspace_size.argtypes = [i, i, i, i, i]
         L.swa_decode_workspace_size.restype = sz
         L.swa_decode.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp]
+        L.swa_decode_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         L.swa_cache_write.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
         L.swa_cache_append.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         L.swa_prefill_cached.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
@@ -62,7 +63,7 @@ def lib():
         L.swa_status_str.restype = ctypes.c_char_p
         for name in ("swa_prefill", "swa_prefill_sinks", "swa_prefill_dilated", "swa_rope",
                      "swa_prefill_rope",
-                     "swa_prefill_cached", "swa_decode",
+                     "swa_prefill_cached", "swa_decode", "swa_decode_noalloc",
                      "swa_cache_write", "swa_cache_append", "swa_longformer",
                      "swa_longformer_proj", "swa_tile_config", "swa_debug_index_mask"):
             getattr(L, name).restype = i
@@ -215,6 +216,31 @@ def decode(q, k_cache, v_cache, slot_pos, cur_pos, scale=None, out=None, workspa
     _check(lib().swa_decode(_dt(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(slot_pos),
                             _ptr(cur_pos), _ptr(o), _ptr(lse), B, W, Hq, Hkv, D, sc, _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(q)), "swa_decode")
+    return (o, lse) if return_lse else o
+
+
+# the size of the library's per-GPU scratch array (SWA_DECODE_NOALLOC_SCRATCH_BYTES)
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc(q, k_cache, v_cache, slot_pos, cur_pos, scale=None, out=None,
+                   return_lse=False):
+    """Ring-cache decode through swa_decode_noalloc: as decode(), with the
+    library's per-GPU scratch array instead of a workspace (only o and lse are
+    allocated here, and not when `out` is given without return_lse)."""
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4)
+    _need(v_cache, "v_cache", 4)
+    _need(slot_pos, "slot_pos", 2)
+    _need(cur_pos, "cur_pos", 1)
+    B, Hq, D = q.shape
+    Hkv, W = k_cache.shape[1], k_cache.shape[2]
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32) if return_lse else None
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib().swa_decode_noalloc(_dt(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(slot_pos),
+                                    _ptr(cur_pos), _ptr(o), _ptr(lse), B, W, Hq, Hkv, D, sc,
+                                    _stream(q)), "swa_decode_noalloc")
     return (o, lse) if return_lse else o
 
 

@@ -2,7 +2,8 @@
 //
 // Every entry point validates all arguments on the host, then launches the
 // gfx950 kernels asynchronously on the caller's stream.  Nothing is allocated
-// and no state is kept between calls.
+// and no state is kept between calls, apart from the per-GPU scratch array of
+// swa_decode_noalloc and its cached device addresses.
 //
 // Tags: [KB] knowledge-base page "Sliding Window Attention" (lizeman.github.io);
 // [G3] "Sliding Window Attention — Gemma 3" study note (ai-engineer-exhaustive);
@@ -10,8 +11,10 @@
 // [ST] "Sliding Window Attention (SWA)" glossary (superteams.ai).
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "swa_internal.h"
@@ -122,6 +125,42 @@ void dilated_xcd_ranges(FwdArgs &a, int BN) {
   for (int x = 1; x <= 8; ++x) a.xcd_off[x] = std::max(a.xcd_off[x], a.xcd_off[x - 1]);
 }
 
+}  // namespace
+}  // namespace swa
+
+// ---- scratch memory of swa_decode_noalloc -------------------------------------
+//
+// One array per GPU, in the library's code object: each device that loads the
+// library holds its own copy until the process ends.  In host code the name
+// `scratch` is only a stand-in; its device address is looked up once per
+// device with hipGetSymbolAddress and kept in scratch_addr, and only that
+// address ever reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[SWA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace swa {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+swa_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SWA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SWA_ERR_UNSUPPORTED;
+  void *p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SWA_ERR_HIP;
+      scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SWA_OK;
+}
 }  // namespace
 }  // namespace swa
 
@@ -464,6 +503,28 @@ swa_status swa_decode(swa_dtype dt, const void *q, const void *k_cache, const vo
   std::memset(&gl, 0, sizeof(gl));
   return hip_status(launch_split(a, true, dt == SWA_F32, d_h, &gl, 0, H_kv,
                                  static_cast<hipStream_t>(stream)));
+}
+
+swa_status swa_decode_noalloc(swa_dtype dt, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *slot_pos,
+                              const int32_t *cur_pos, void *o, float *lse, int B, int W, int H_q,
+                              int H_kv, int d_h, float scale, void *stream) {
+  // the checks of swa_decode, before any HIP call
+  if (!dt_ok(dt) || !q || !k_cache || !v_cache || !slot_pos || !cur_pos || !o)
+    return SWA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(slot_pos, 4) || !aligned(cur_pos, 4) || (lse && !aligned(lse, 4)))
+    return SWA_ERR_INVALID;
+  if (B < 1 || W < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || !scale_ok(scale))
+    return SWA_ERR_INVALID;
+  if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
+  if (swa_decode_workspace_size(B, H_q, H_kv, W, d_h) > SWA_DECODE_NOALLOC_SCRATCH_BYTES)
+    return SWA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const swa_status st = scratch_for_current_device(&ws);
+  if (st != SWA_OK) return st;
+  return swa_decode(dt, q, k_cache, v_cache, slot_pos, cur_pos, o, lse, B, W, H_q, H_kv, d_h,
+                    scale, ws, SWA_DECODE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 swa_status swa_cache_write(swa_dtype dt, const void *k_new, const void *v_new, const int32_t *pos,
