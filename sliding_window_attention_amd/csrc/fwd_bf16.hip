@@ -1096,42 +1096,54 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // product through the partner lane; the state (m, l, O) is updated as for a
   // tile of one key, with P in fp32.  `take` drops keys the band already
   // counted (and rows past the end).
+  // The products run on v_dot2_f32_bf16 straight from the packed bf16 q, k
+  // and v (no unpacking); the weight is rounded to bf16 first, as the band's
+  // P is, and the row sum takes that rounded weight.
   auto extra_key = [&](const char *kr, const char *vr, bool take) {
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS_QK; ++ks) {
       const U4 kk = *reinterpret_cast<const U4 *>(kr + (ks * 16 + lh * 8) * 2);
+      // (through the U4 struct: indexing a bit-cast ext_vector of uint32 here
+      // made this compiler read word 0 for every w)
+      const U4 qw = __builtin_bit_cast(U4, qf[ks]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        part = fmaf((float)qf[ks][2 * w], __uint_as_float(kk.w[w] << 16), part);
-        part = fmaf((float)qf[ks][2 * w + 1], __uint_as_float(kk.w[w] & 0xffff0000u), part);
-      }
+      for (int w = 0; w < 4; ++w)
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw.w[w]),
+                                               __builtin_bit_cast(bf16x2, kk.w[w]), part, false);
     }
     const float dot = xhalf_add(part);
     const float sg = take ? dot * a.sl2 : -INFINITY;
     rescale(sg);
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    const float pg = take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f;
-    if (lh == 0) l_run += pg;  // l_run holds per-lane shares until the epilogue
+    const __bf16 pb = (__bf16)(take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f);
+    if (lh == 0) l_run += (float)pb;  // l_run holds per-lane shares until the epilogue
+    const bf16x2 p_lo = {pb, (__bf16)0.f}, p_hi = {(__bf16)0.f, pb};
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const uint2 vv = *reinterpret_cast<const uint2 *>(vr + (db * 32 + 8 * g4 + 4 * lh) * 2);
-        acc_o[db][4 * g4 + 0] = fmaf(pg, __uint_as_float(vv.x << 16), acc_o[db][4 * g4 + 0]);
-        acc_o[db][4 * g4 + 1] = fmaf(pg, __uint_as_float(vv.x & 0xffff0000u), acc_o[db][4 * g4 + 1]);
-        acc_o[db][4 * g4 + 2] = fmaf(pg, __uint_as_float(vv.y << 16), acc_o[db][4 * g4 + 2]);
-        acc_o[db][4 * g4 + 3] = fmaf(pg, __uint_as_float(vv.y & 0xffff0000u), acc_o[db][4 * g4 + 3]);
+        const bf16x2 v0 = __builtin_bit_cast(bf16x2, vv.x), v1 = __builtin_bit_cast(bf16x2, vv.y);
+        acc_o[db][4 * g4 + 0] = __builtin_amdgcn_fdot2_f32_bf16(v0, p_lo, acc_o[db][4 * g4 + 0], false);
+        acc_o[db][4 * g4 + 1] = __builtin_amdgcn_fdot2_f32_bf16(v0, p_hi, acc_o[db][4 * g4 + 1], false);
+        acc_o[db][4 * g4 + 2] = __builtin_amdgcn_fdot2_f32_bf16(v1, p_lo, acc_o[db][4 * g4 + 2], false);
+        acc_o[db][4 * g4 + 3] = __builtin_amdgcn_fdot2_f32_bf16(v1, p_hi, acc_o[db][4 * g4 + 3], false);
       }
   };
   if constexpr (MODE == kSymmetric) {
     // global keys; one already inside the row's (dilated) window is skipped
     if (a.G > 0 && has_rows) {
-      const int i_abs = rho + dil * my_row;
       for (int u = 0; u < a.G; ++u) {
-        const int g = gl.idx[b * a.G + u];
+        // g is in the dilated window of row rho + dil*my_row iff it lies in
+        // the row's residue class (a wave-uniform test) at class index c
+        // with |my_row - c| <= r
+        const int dg = uni(gl.idx[b * a.G + u] - rho);
+        const bool same_class = dg % dil == 0;
+        const int c = dg / dil;
+        const bool in_win = same_class && my_row - c <= a.W && c - my_row <= a.W;
         extra_key(gkv + u * Gm::ROWB, gkv + (kValuGlobals + u) * Gm::ROWB,
-                  my_row < n_cls && !dilated_in(i_abs, g, a.W, dil));
+                  my_row < n_cls && !in_win);
       }
     }
   }

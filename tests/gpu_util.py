@@ -9,7 +9,12 @@ import torch
 # float32 path (max abs error on the outputs).
 TOL_BF16 = 2e-2
 TOL_F32 = 1e-5
-TOL_LSE_BF16 = 2e-3   # lse sees exact bf16 products summed in fp32
+# lse, bf16 path: the scores are exact bf16 products summed in fp32, but the
+# row sum l adds the weights p rounded to bf16 (the ones the P.V product uses),
+# each off by at most 2^-8 relative, so ln l may be off by ln(1 + 2^-8) =
+# 3.9e-3 when a row's few weights all round the same way (many-key rows average
+# out far below that); exp2 / log2 and fp32 sums add ~1e-6.
+TOL_LSE_BF16 = 4e-3
 TOL_LSE_F32 = 1e-5
 # lse when q = 0: every score is 0, every weight is exactly 1 (2^0, also in
 # bf16), so the row sum l is the integer |S_t| held exactly in fp32 (< 2^24)
