@@ -145,8 +145,9 @@ swa_status swa_prefill_rope(swa_dtype dt, const void *q, const void *k, const vo
  * writes the current token into its slot first (swa_cache_write) and then calls
  * swa_decode.  Slot j is attended iff slot_pos[b][j] >= 0 and
  * cur_pos[b]-W < slot_pos[b][j] <= cur_pos[b]; slots holding stale or future
- * positions and empty slots (negative) are ignored.  A request with no valid
- * slot gets o = 0 and lse = -inf.
+ * positions and empty slots (negative) are ignored, whatever bits their keys
+ * and values hold (NaN or Inf included).  A request with no valid slot gets
+ * o = 0 and lse = -inf.
  *   q, o             : [B, H_q, d_h]
  *   k_cache, v_cache : [B, H_kv, W, d_h]
  *   slot_pos         : [B, W] int32        cur_pos : [B] int32   (device)
@@ -219,6 +220,9 @@ swa_status swa_cache_append(swa_dtype dt, const void *k_new, const void *v_new,
  * With n_sink > 0, slots holding one of the first n_sink positions (p <= q_pos)
  * are attended too; sink_logit as in swa_prefill_sinks (NULL = none).
  * A query with no valid slot gets o = 0 and lse = -inf (lse = z with a sink score).
+ * Empty slots (negative position) may hold any bits (NaN or Inf included);
+ * every other slot must hold finite keys and values, since a slot outside one
+ * query's window may be inside another's of the same chunk.
  *   q, o             : [B, L, H_q, d_h]
  *   k_cache, v_cache : [B, H_kv, S, d_h]
  *   slot_pos         : [B, S] int32     q_pos : [B, L] int32, >= 0  (device)
