@@ -1327,8 +1327,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int mode, int D, const GlobalList *
     for (int x = 0; x < 8; ++x) most = std::max(most, a.xcd_off[x + 1] - a.xcd_off[x]);
     nblk = 8 * most;
   }
-  constexpr int NWC = SWA_FWD_WAVES;
-  if (a.NW != fwd_waves(mode)) return hipErrorInvalidValue;
+  constexpr int NWC = kFwdWaves;
+  if (a.NW != kFwdWaves) return hipErrorInvalidValue;
   dim3 grid(nblk), block(64 * a.NW);
   if (mode == kCausal) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, kCausal, NWC>), grid, block, 0, st, a, *gl);

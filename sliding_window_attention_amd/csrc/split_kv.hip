@@ -30,9 +30,6 @@ struct alignas(16) U4 {
   uint32_t w[4];
 };
 
-__device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-
 // 8 consecutive elements starting at p, widened to fp32
 template <bool F32>
 __device__ inline void load8(const void *p, float *out) {
@@ -42,11 +39,12 @@ __device__ inline void load8(const void *p, float *out) {
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
   } else {
+    // bf16 -> fp32: the 16 bits become the high half of the fp32 word
     const U4 u = *reinterpret_cast<const U4 *>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = bf_lo(u.w[i]);
-      out[2 * i + 1] = bf_hi(u.w[i]);
+      out[2 * i] = __uint_as_float(u.w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(u.w[i] & 0xffff0000u);
     }
   }
 }

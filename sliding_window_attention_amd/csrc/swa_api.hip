@@ -185,9 +185,9 @@ swa_status swa_tile_config(int entry, int H_q, int H_kv, int d_h, int *BM, int *
   if (!BM || !BN || H_q < 1 || H_kv < 1 || H_q % H_kv) return SWA_ERR_INVALID;
   if (!d_ok(d_h)) return SWA_ERR_UNSUPPORTED;
   if (entry == 'p') {
-    *BM = kRowsPerWave * fwd_waves(kCausal) / prefill_pack(H_q, H_kv);
+    *BM = kRowsPerWave * kFwdWaves / prefill_pack(H_q, H_kv);
   } else if (entry == 'l') {
-    *BM = kRowsPerWave * fwd_waves(kSymmetric);
+    *BM = kRowsPerWave * kFwdWaves;
   } else {
     return SWA_ERR_INVALID;
   }
@@ -255,7 +255,7 @@ swa_status swa_prefill_sinks(swa_dtype dt, const void *q, const void *k, const v
   a.group = H_q / H_kv;
   const int mode = (n_sink > 0 || sink_logit) ? kCausalSink : kCausal;
   a.P = prefill_pack(H_q, H_kv);
-  a.NW = fwd_waves(mode);
+  a.NW = kFwdWaves;
   a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (T + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
@@ -313,7 +313,7 @@ swa_status swa_prefill_dilated(swa_dtype dt, const void *q, const void *k, const
   for (int h = 0; h < H_q && P > 1; ++h)
     if (dilation[h] != dilation[h - h % P]) P = 1;
   a.P = P;
-  a.NW = fwd_waves(kCausalDil);
+  a.NW = kFwdWaves;
   a.BM = kRowsPerWave * a.NW / P;
   a.n_hg = H_q / P;
   if (a.n_hg > kMaxHeadsLF) return SWA_ERR_UNSUPPORTED;
@@ -377,7 +377,7 @@ swa_status swa_prefill_rope(swa_dtype dt, const void *q, const void *k, const vo
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
   a.P = prefill_pack(H_q, H_kv);
-  a.NW = fwd_waves(kCausal);
+  a.NW = kFwdWaves;
   a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (T + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
@@ -427,7 +427,7 @@ swa_status swa_prefill_cached(swa_dtype dt, const void *q, const void *k_cache,
   a.sl2 = scale * kLog2e;
   a.group = H_q / H_kv;
   a.P = prefill_pack(H_q, H_kv);
-  a.NW = fwd_waves(kRing);
+  a.NW = kFwdWaves;
   a.BM = kRowsPerWave * a.NW / a.P;
   a.n_qt = (L + a.BM - 1) / a.BM;
   a.n_hg = H_q / a.P;
@@ -613,7 +613,7 @@ swa_status longformer_impl(swa_dtype dt, const void *q, const void *k, const voi
   a.sl2 = scale * kLog2e;
   a.group = 1;
   a.P = 1;
-  a.NW = fwd_waves(kSymmetric);
+  a.NW = kFwdWaves;
   a.BM = kRowsPerWave * a.NW;
   a.G = G;
   long long tiles = 0;

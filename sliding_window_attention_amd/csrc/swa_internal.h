@@ -141,13 +141,12 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
 __host__ __device__ constexpr int key_tile(int D) { return D == 64 ? 64 : 32; }
 constexpr int kRowsPerWave = 32; // query rows per wave (one 32x32 MFMA block)
 
-// Waves per workgroup of the bf16 kernels.  Every wave of a workgroup reads
-// the same staged K/V tiles, so more waves per workgroup means fewer bytes
-// copied into LDS per FLOP.  Causal prefill runs 12 waves (one workgroup per
-// CU, three waves per SIMD) or 4; symmetric mode 4.
-#ifndef SWA_FWD_WAVES
-#define SWA_FWD_WAVES 4
-#endif
+// Waves per workgroup of the bf16 banded kernels: four, one per SIMD, with
+// three workgroups per CU at the causal kernels' register count.  Every wave
+// of a workgroup reads the same staged K/V tiles, so larger workgroups would
+// copy fewer bytes into LDS per FLOP, but their waves share SIMDs behind one
+// barrier per tile and ran slower.
+constexpr int kFwdWaves = 4;
 
 
 // Heads packed into one workgroup for the causal kernel: waves of one
@@ -246,10 +245,6 @@ enum FwdMode {
   kCausalDil = 5
 };
 
-// Waves per workgroup of the banded kernel for a window family.
-inline int fwd_waves(int mode) {
-  return (mode == kSymmetric || mode == kSymmetricProj) ? 4 : SWA_FWD_WAVES;
-}
 
 struct GlobalList {
   int idx[kMaxGlobalsLF];  // [B][G] positions
