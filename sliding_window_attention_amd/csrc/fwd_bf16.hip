@@ -5,8 +5,8 @@
 // "The Mechanism": out-of-window key/value blocks are skipped).  Each wave owns
 // 32 query rows of one head; the waves of a workgroup share one key/value head
 // (P query heads x NW/P row blocks), so every staged K/V tile feeds NW waves.
-// A wave skips the staged tiles outside its own rows' band.  Per key tile of
-// 32 columns:
+// A wave skips the staged tiles outside its own rows' band.  Key tiles are 32
+// keys at d_h = 128 and 64 at d_h = 64; per 32-key block of a tile:
 //
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A), Q in VGPRs (B)
 //   mask             only on tiles the schedule marks as partial

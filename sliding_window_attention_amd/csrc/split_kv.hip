@@ -2,12 +2,14 @@
 // global rows of Longformer attention.
 //
 // Both are HBM-bound streams over keys.  The keys of one (batch, key/value
-// head) are cut into S chunks; one workgroup per chunk computes, for every
-// query sharing that head, the partial softmax state (max m, sum l and the
-// unnormalised sum of p*v) and writes it to the workspace.  A second kernel
-// merges the S partials: with M = max_s m_s, o = sum_s 2^(m_s-M) acc_s /
-// sum_s 2^(m_s-M) l_s, which equals the softmax over the union of the chunks
-// exactly up to rounding (softmax over a disjoint union).
+// head) are cut into S chunks; each chunk yields, for every query sharing that
+// head, the partial softmax state (max m, sum l and the unnormalised sum of
+// p*v), and the S partials merge as: with M = max_s m_s, o = sum_s 2^(m_s-M)
+// acc_s / sum_s 2^(m_s-M) l_s, which equals the softmax over the union of the
+// chunks exactly up to rounding (softmax over a disjoint union).  bf16 decode
+// runs the S chunks as the waves of one workgroup and merges them in LDS; the
+// other uses give each chunk a workgroup that writes its state to the
+// workspace, merged by a second kernel.
 //
 // Decode mask: slot j is attended iff its stored absolute position p satisfies
 // p >= 0 and cur-W < p <= cur ([KB] §2 "KV cache": token p lives in slot p mod W;
