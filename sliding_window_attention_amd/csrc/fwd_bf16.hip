@@ -771,6 +771,10 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc_o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  // exponent reference (m_run, or 0 while m_run = -inf) and the raw-score
+  // threshold above which a row triggers the lazy rescale, (m_run + kLazy) /
+  // sl2; both change only when m_run does
+  float m_use = 0.f, m_thr = -INFINITY;
   const int my_row = row0 + lq;
 
   // ---- building blocks.  Accumulator element (kb, e) of S^T holds key
@@ -787,33 +791,36 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       }
   };
   // row max over the tile, in log2 units (sl2 = scale * log2 e)
+  // row max over the tile in raw score units: three-input max chains, then
+  // the partner half-wave
   auto rowmax = [&](const f32x16 *sv) {
-    float mx = fmaxf(sv[0][0], sv[0][1]);
+    float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), sv[0][2]);
 #pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[0][e], sv[0][e + 1]));
+    for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, sv[0][e]), sv[0][e + 1]);
+    mx = fmaxf(mx, sv[0][15]);
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sv[kb][e], sv[kb][e + 1]));
-    return xhalf_max(mx) * a.sl2;
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, sv[kb][e]), sv[kb][e + 1]);
+    return xhalf_max(mx);
   };
   // The reference max m_run is only raised when some row of the wave would
   // otherwise see p = 2^(s - m_run) above 2^kLazy; l and O share the same
-  // reference, so the result is unchanged and O is rarely rescaled.
+  // reference, so the result is unchanged and O is rarely rescaled.  mx is in
+  // raw score units.
   auto rescale = [&](float mx) {
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
-      const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
+      const float m_new = fmaxf(m_run, mx * a.sl2);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i) acc_o[i] *= alpha;
       m_run = m_new;
+      m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      m_thr = (m_run == -INFINITY) ? -INFINITY : (m_run + kLazy) / a.sl2;
     }
   };
-  // p = 2^(s*sl2 - m), row sum into l, P -> bf16 (RNE) packed as the B
-  // operands of the four PV k-steps
   auto exp_pack = [&](f32x16 *sv, U4 *pu) {
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -1113,10 +1120,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
                                                __builtin_bit_cast(bf16x2, kk.w[w]), part, false);
     }
     const float dot = xhalf_add(part);
-    const float sg = take ? dot * a.sl2 : -INFINITY;
-    rescale(sg);
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    const __bf16 pb = (__bf16)(take ? __builtin_amdgcn_exp2f(sg - m_use) : 0.f);
+    rescale(take ? dot : -INFINITY);
+    const __bf16 pb = (__bf16)(take ? __builtin_amdgcn_exp2f(fmaf(dot, a.sl2, -m_use)) : 0.f);
     if (lh == 0) l_run += (float)pb;  // l_run holds per-lane shares until the epilogue
     const bf16x2 p_lo = {pb, (__bf16)0.f}, p_hi = {(__bf16)0.f, pb};
 #pragma unroll
