@@ -791,8 +791,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       }
   };
   // row max over the tile, in log2 units (sl2 = scale * log2 e)
-  // row max over the tile in raw score units: three-input max chains, then
-  // the partner half-wave
+  // this lane's share of its row max over the tile (its half of the keys), in
+  // raw score units: three-input max chains
   auto rowmax = [&](const f32x16 *sv) {
     float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), sv[0][2]);
 #pragma unroll
@@ -802,14 +802,17 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     for (int kb = 1; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, sv[kb][e]), sv[kb][e + 1]);
-    return xhalf_max(mx);
+    return mx;
   };
   // The reference max m_run is only raised when some row of the wave would
   // otherwise see p = 2^(s - m_run) above 2^kLazy; l and O share the same
-  // reference, so the result is unchanged and O is rarely rescaled.  mx is in
-  // raw score units.
-  auto rescale = [&](float mx) {
-    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
+  // reference, so the result is unchanged and O is rarely rescaled.  mx is a
+  // lane's share of its row max in raw score units: a row's max passes the
+  // threshold iff one of its two halves does, so the test needs no exchange
+  // with the partner half-wave; the rescale takes the whole row's max.
+  auto rescale = [&](float mx_half) {
+    if (__builtin_amdgcn_ballot_w64(mx_half > m_thr) != 0) {
+      const float mx = xhalf_max(mx_half);
       const float m_new = fmaxf(m_run, mx * a.sl2);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
