@@ -908,10 +908,10 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     const bool live = (lane % BN) < n_in && sp >= 0 && sp <= pos_hi &&
                       ((long long)sp > (long long)pos_lo - a.W || sp < a.n_sink);
     if (__builtin_amdgcn_ballot_w64(live) == 0) return 0;
-    int lo = sp, hi = sp;
-    lane_minmax<(BN > 32)>(lo, hi);  // with 32 slots both half-waves hold them all
-    const bool full = n_in == BN && uni(lo) >= 0 &&
-                      (long long)uni(lo) > (long long)pos_hi - a.W && uni(hi) <= pos_lo;
+    // every slot in the window of every row (with 32 slots both half-waves
+    // hold them all)
+    const bool all_in = sp >= 0 && (long long)sp > (long long)pos_hi - a.W && sp <= pos_lo;
+    const bool full = n_in == BN && __builtin_amdgcn_ballot_w64(all_in) == ~0ull;
     return full ? 1 : 2;
   };
   // Ring mask: slot k of the tile (k < S) is attended iff its position p has
