@@ -636,8 +636,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   tr.lo = uni(tr.lo);
   tr.hi = uni(tr.hi);
   const int n_win = tr.hi - tr.lo + 1;
-  // extra tiles after the window: global keys (symmetric), or key tile 0 for
-  // the sink tokens when the window tiles do not reach it (causal)
+  // extra tiles after the window: the global keys when they have projections
+  // of their own (sink tokens and shared-projection globals are staged apart)
   const int n_glob = GPROJ ? ceil_div(a.G, BN) : 0;
   const int n_tiles = n_win + n_glob;
   // this wave's valid rows [row0, w_last] and the window tiles they need
@@ -651,6 +651,41 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   wr.lo = uni(wr.lo);
   wr.hi = uni(wr.hi);
   const bool has_rows = w_last >= row0;
+  // Per tile, one unsigned compare each: window tile j is computed iff
+  // j - jc_lo <= jc_span, and needs no mask iff j - jf_lo <= jf_span (the
+  // full tiles of the wave's rows, a sub-range of its window tiles).
+  int jc_lo = 1 << 30, jf_lo = 1 << 30;
+  unsigned jc_span = 0, jf_span = 0;
+  if (has_rows) {
+    jc_lo = wr.lo - tr.lo;
+    jc_span = (unsigned)(wr.hi - wr.lo);
+    if constexpr (!RING) {
+      TileRange fr;
+      if constexpr (!SYM) fr = causal_full_range(row0, w_last, a.W, BN, n_cls);
+      else fr = sym_full_range(row0, w_last, a.W, BN, n_cls);
+      fr.lo = max(fr.lo, wr.lo);
+      fr.hi = min(fr.hi, wr.hi);
+      if (fr.lo <= fr.hi) {
+        jf_lo = fr.lo - tr.lo;
+        jf_span = (unsigned)(fr.hi - fr.lo);
+      }
+    }
+  }
+  // the 32-key blocks every row of the wave attends in full (64-key tiles)
+  TileRange fb{1 << 30, 1 << 30};
+  if constexpr (!RING && KB > 1) {
+    if (has_rows) {
+      const TileRange f = SYM ? sym_full_range(row0, w_last, a.W, 32, n_cls)
+                              : causal_full_range(row0, w_last, a.W, 32, n_cls);
+      if (f.lo <= f.hi) fb = f;
+    }
+    fb.lo = uni(fb.lo);
+    fb.hi = uni(fb.hi);
+  }
+  jc_lo = uni(jc_lo);
+  jf_lo = uni(jf_lo);
+  jc_span = (unsigned)uni((int)jc_span);
+  jf_span = (unsigned)uni((int)jf_span);
 
   // -------- DMA addressing.  A stage takes 2*NI wave instructions of 1 KB:
   // instruction i < NI copies K rows i*RPI .. i*RPI+RPI-1, instruction NI + i
@@ -688,11 +723,13 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // Four copies per wave, the first two K rows and the last two V rows (four
   // waves): a whole window tile goes out as one branch-free block.
   constexpr bool KV4 = NSLOT == 4 && NSLOT * NW == 2 * Gm::NI && Gm::NI == 2 * NW;
+  // window tiles j <= jw_hi hold BN valid key rows
+  const int jw_hi = uni(min(n_keyrows / BN - 1, tr.hi) - tr.lo);
   auto issue = [&](int j, uint32_t stage) {
-    const int kt = (j < n_win) ? tr.lo + j : 0;  // key tile (sink tile: 0)
-    const bool whole = (j < n_win || !SYM) && kt * BN + BN <= n_keyrows;
+    const int kt = (j < n_win) ? tr.lo + j : 0;  // key tile (0 past the window)
+    const bool whole = (j < n_win) ? j <= jw_hi : (!SYM && BN <= n_keyrows);
     const long long base = (k_rho + (long long)kt * BN * k_rowstride) * 2;
-    if (KV4 && whole && j < n_win) {
+    if (KV4 && j <= jw_hi) {
       const char *kt8 = kb8 + base;
       dma_kv4<NW * 1024>(kt8, kt8 + d_v, loff, stage + (uint32_t)wave * 1024u);
     } else {
@@ -880,12 +917,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     return m;
   };
   // every (valid row of this wave, key) pair of window tile j attended?
-  auto tile_full = [&](int j) {
-    if (j >= n_win) return false;  // tiles of global keys are always masked
-    const int kj = tr.lo + j;
-    if constexpr (!SYM) return causal_tile_full(row0, w_last, kj, BN, a.W, n_cls);
-    else return sym_tile_full(row0, w_last, kj, BN, a.W, n_cls);
-  };
+  // (tiles of global keys, j >= n_win, lie outside the range: always masked)
+  auto tile_full = [&](int j) { return (unsigned)(j - jf_lo) <= jf_span; };
   // Ring mode: this lane's query position and the wave's position range.
   int my_pos = 0, pos_lo = 0, pos_hi = 0;
   if constexpr (RING) {
@@ -989,9 +1022,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
         if constexpr (KB > 1) {
           // a 32-key block inside every row's window needs no mask
           const int blk = (tr.lo + j) * (BN / 32) + kb;
-          const bool full = SYM ? sym_tile_full(row0, w_last, blk, 32, a.W, n_cls)
-                                : causal_tile_full(row0, w_last, blk, 32, a.W, n_cls);
-          if (full) continue;
+          if ((unsigned)(blk - fb.lo) <= (unsigned)(fb.hi - fb.lo)) continue;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -1025,20 +1056,18 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   static_assert((2 * Gm::NI) % NW == 0, "every wave issues the same number of copies");
   auto step = [&](int j, auto stage) {
     constexpr int st = decltype(stage)::value;
-    wait_dma_keep(min(n_tiles - 1 - j, NST - 2) * NCOPY);
+    wait_dma_keep(NST == 2 ? 0 : min(n_tiles - 1 - j, NST - 2) * NCOPY);
     __syncthreads();
     if (j + NST - 1 < n_tiles) issue(j + NST - 1, a_s0 + (uint32_t)(((st + NST - 1) % NST) * STAGE_B));
-    const int kj = tr.lo + j;
-    // a wave computes the tiles of its rows' band, the extra tiles, and key
-    // tile 0 when sink tokens live there
+    // a wave computes the tiles of its rows' band and the tiles of global keys
     char *ks = smem + st * STAGE_B;
     int rc = 1;  // ring mode: tile class (0 = nothing attended, skip)
     if constexpr (RING) {
       ring_zero_holes(ks, j);
       rc = has_rows ? ring_class(ks, j) : 0;
     }
-    if (has_rows && rc != 0 &&
-        (j >= n_win || (kj >= wr.lo && kj <= wr.hi))) {
+    const bool comp = (n_glob > 0 && j >= n_win) ? has_rows : (unsigned)(j - jc_lo) <= jc_span;
+    if (rc != 0 && comp) {
       f32x16 sv[KB];
       U4 pu[PK];
       qk(ks, sv);

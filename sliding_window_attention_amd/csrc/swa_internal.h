@@ -49,7 +49,7 @@ __host__ __device__ inline bool dilated_in(int i, int j, int r, int dil) {
 __host__ __device__ inline void row_key_bounds(bool symmetric, int i, int w_or_r, int n, int *lo,
                                                int *hi) {
   *lo = symmetric ? i - w_or_r : i - w_or_r + 1;
-  const int h = symmetric ? i + w_or_r : i;
+  const int h = symmetric ? (i >= n - 1 - w_or_r ? n - 1 : i + w_or_r) : i;  // no overflow
   *hi = h < n - 1 ? h : n - 1;
 }
 
@@ -70,22 +70,40 @@ __host__ __device__ inline TileRange causal_tile_range(int t0, int t1, int W, in
   return {s_lo / BN, t1 / BN};
 }
 
+// The tiles needing no mask are a contiguous range too (empty when lo > hi):
+// tile kj (columns s0 = kj*BN .. s1 = s0+BN-1) is full iff s1 <= t0 (every
+// column at or before the first row), s0 > t1 - W (inside the last row's
+// window) and s1 < n.
+__host__ __device__ inline TileRange causal_full_range(int t0, int t1, int W, int BN, int n) {
+  const int x = t1 - W + 1;  // first column of the last row's window
+  const int lo = x <= 0 ? 0 : (x + BN - 1) / BN;
+  const int hi = ((t0 + 1 < n ? t0 + 1 : n) / BN) - 1;
+  return {lo, hi};
+}
+
 __host__ __device__ inline bool causal_tile_full(int t0, int t1, int kj, int BN, int W, int n) {
-  const int s0 = kj * BN, s1 = s0 + BN - 1;
-  return s1 <= t0 && s0 > t1 - W && s1 < n;
+  const TileRange f = causal_full_range(t0, t1, W, BN, n);
+  return kj >= f.lo && kj <= f.hi;
 }
 
 __host__ __device__ inline TileRange sym_tile_range(int i0, int i1, int r, int n, int BN) {
   int s_lo = i0 - r;
   if (s_lo < 0) s_lo = 0;
-  int s_hi = i1 + r;
-  if (s_hi > n - 1) s_hi = n - 1;
+  const int s_hi = i1 >= n - 1 - r ? n - 1 : i1 + r;  // no overflow for large r
   return {s_lo / BN, s_hi / BN};
 }
 
+// Full tiles: s1 - i0 <= r, i1 - s0 <= r and s1 < n (empty when lo > hi).
+__host__ __device__ inline TileRange sym_full_range(int i0, int i1, int r, int BN, int n) {
+  const int x = i1 - r;  // first column within r of the last row
+  const int lo = x <= 0 ? 0 : (x + BN - 1) / BN;
+  const int top = i0 >= n - 1 - r ? n : i0 + r + 1;  // one past the first row's last column
+  return {lo, top / BN - 1};
+}
+
 __host__ __device__ inline bool sym_tile_full(int i0, int i1, int kj, int BN, int r, int n) {
-  const int s0 = kj * BN, s1 = s0 + BN - 1;
-  return s1 - i0 <= r && i1 - s0 <= r && s1 < n;
+  const TileRange f = sym_full_range(i0, i1, r, BN, n);
+  return kj >= f.lo && kj <= f.hi;
 }
 
 // ---------------------------------------------------------------- residue classes

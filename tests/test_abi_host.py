@@ -279,6 +279,16 @@ def test_symmetric_schedule_matches_bruteforce(T, r, BM, BN):
     assert bd.band_tiles(bd.SWA_MODE_SYMMETRIC, T, r, BM, BN) == _bruteforce_triples("symmetric", T, r, BM, BN)
 
 
+@pytest.mark.parametrize("T", [1, 7, 100])
+def test_schedule_with_huge_window(T):
+    # a window or radius past the sequence (up to INT_MAX, where r + i would
+    # overflow 32-bit arithmetic) is full attention: same plan as W = T, r = T
+    big = 2**31 - 1
+    for BM, BN in ((16, 16), (32, 64)):
+        assert bd.band_tiles(bd.SWA_MODE_CAUSAL, T, big, BM, BN) == _bruteforce_triples("causal", T, T, BM, BN)
+        assert bd.band_tiles(bd.SWA_MODE_SYMMETRIC, T, big, BM, BN) == _bruteforce_triples("symmetric", T, T, BM, BN)
+
+
 def test_schedule_at_kernel_tiling_small():
     # the kernels' real tile sizes on shapes small enough for brute force
     for (Hq, Hkv) in ((32, 8), (32, 16), (4, 4)):

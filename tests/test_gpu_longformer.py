@@ -65,6 +65,26 @@ def test_longformer_f32(case):
     assert max_err(lse, rl) <= TOL_LSE_F32
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", [(1, 200, 2, 64, [1, 3], [[0, 150]]),
+                                  (2, 129, 2, 128, [2, 1], [])], ids=str)
+def test_longformer_radius_past_the_sequence(case, dtype):
+    # r = 2^31 - 1 (where i + r leaves 32-bit range) reaches every key of the
+    # row's class, as r = T does; the oracle runs at r = T
+    B, T, H, D, dil, gl = case
+    c = inp.LongformerCase(B=B, T=T, H=H, D=D, r=T, dilation=dil,
+                           globals_=gl[0] if gl else [], dtype=dtype, seed=5 + T)
+    q, k, v, dl, _ = inp.longformer_inputs(c)
+    g = np.repeat(np.asarray(gl, dtype=np.int32).reshape(1, -1), B, axis=0) if gl else None
+    banner(f"longformer {dtype} r=2^31-1 {case}")
+    o, lse = bd.longformer(dev(q), dev(k), dev(v), 2**31 - 1, dl, g, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.swa_longformer(inp.widen(q), inp.widen(k), inp.widen(v), T, dl, g)
+    tol, tol_lse = (TOL_BF16, TOL_LSE_BF16) if dtype == "bf16" else (TOL_F32, TOL_LSE_F32)
+    assert max_err(host(o), ro) <= tol
+    assert max_err(host(lse), rl) <= tol_lse
+
+
 def _class_blocks(T, dil, n=32):
     return sum(-(-len(range(rho, T, dil)) // n) for rho in range(dil))
 
@@ -212,9 +232,12 @@ def test_index_readout_printed_tables(dtype, name, r, dil, gl, total):
     (0, 300, 70, 1, []), (0, 257, 1, 1, []), (0, 100, 500, 1, []),
     (1, 300, 20, 1, []), (1, 300, 20, 3, [0, 77, 299]), (1, 257, 64, 2, [128]),
     (1, 16, 2, 2, []), (1, 16, 2, 1, [0, 8]),
+    # a window or radius of 2^31 - 1 covers everything, as w = T does
+    (0, 100, 2**31 - 1, 1, []), (1, 100, 2**31 - 1, 3, [5]),
 ])
 def test_device_predicate_matches_oracle(mode, T, w, dil, gl):
     banner(f"debug mask mode={mode} T={T} w={w} dil={dil}")
     m = bd.debug_index_mask(mode, T, w, dil, gl).cpu().numpy().astype(bool)
+    w = min(w, T)
     want = oracle.causal_mask(T, w) if mode == 0 else oracle.longformer_mask(T, w, dil, gl)
     assert np.array_equal(m, want)

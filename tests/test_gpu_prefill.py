@@ -55,6 +55,22 @@ def test_prefill_f32(case):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", [(1, 300, 4, 2, 128), (1, 257, 8, 2, 64)], ids=str)
+def test_prefill_window_past_int_range(case, dtype):
+    # W = 2^31 - 1 is full causal attention: the oracle runs at W = T
+    B, T, Hq, Hkv, D = case
+    c = inp.PrefillCase(B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, W=T, dtype=dtype, seed=3 + T)
+    q, k, v = inp.prefill_inputs(c)
+    banner(f"prefill {dtype} W=2^31-1 {case}")
+    o, lse = bd.prefill(dev(q), dev(k), dev(v), 2**31 - 1, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.swa_prefill(inp.widen(q), inp.widen(k), inp.widen(v), T)
+    tol, tol_lse = (TOL_BF16, TOL_LSE_BF16) if dtype == "bf16" else (TOL_F32, TOL_LSE_F32)
+    assert max_err(host(o), ro) <= tol
+    assert max_err(host(lse), rl) <= tol_lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("T,D,Hq,Hkv,W", [(16, 64, 1, 1, 1), (16, 64, 1, 1, 4), (16, 64, 1, 1, 16),
                                           (16, 64, 1, 1, 20), (128, 128, 4, 1, 1),
                                           (128, 128, 4, 1, 63), (128, 128, 4, 1, 64),
