@@ -471,12 +471,14 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // NST stages, each a row-major K tile followed by a V tile (swizzled
   // chunks); copies run NST-1 tiles ahead of the compute.  After the loop the
   // same memory stages the output rows.
-  // ring mode: the tile's slot positions follow its V tile (256 bytes)
-  constexpr int SP_OFF = 2 * Gm::TILE_B;
-  constexpr int STAGE_B = 2 * Gm::TILE_B + (RING ? 256 : 0);
+  constexpr int STAGE_B = 2 * Gm::TILE_B;
   constexpr int NST = SYM ? SWA_SYM_STAGES : 2;
+  // ring mode: the slot positions of stage st sit at byte 256 st, ahead of
+  // the stages, so every read of them is one base register plus an immediate
+  constexpr int SPA = RING ? 1024 : 0;
+  static_assert(!RING || NST * 256 <= SPA, "slot positions fit ahead of the stages");
   constexpr int OST_B = NW * kRowsPerWave * D * 2;
-  constexpr int SMEM_B = (NST * STAGE_B > OST_B) ? NST * STAGE_B : OST_B;
+  constexpr int SMEM_B = (SPA + NST * STAGE_B > OST_B) ? SPA + NST * STAGE_B : OST_B;
   // symmetric mode: K rows then V rows of the (at most kValuGlobals) global
   // keys, staged once for the after-the-band pass
   // (causal sink mode: the K rows then V rows of the sink tokens, likewise)
@@ -725,7 +727,9 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   constexpr bool KV4 = NSLOT == 4 && NSLOT * NW == 2 * Gm::NI && Gm::NI == 2 * NW;
   // window tiles j <= jw_hi hold BN valid key rows
   const int jw_hi = uni(min(n_keyrows / BN - 1, tr.hi) - tr.lo);
-  auto issue = [&](int j, uint32_t stage) {
+  const uint32_t a_s0 = lds_addr(smem) + (uint32_t)SPA;  // the stages
+  auto issue = [&](int j, int si) {  // into stage si
+    const uint32_t stage = a_s0 + (uint32_t)(si * STAGE_B);
     const int kt = (j < n_win) ? tr.lo + j : 0;  // key tile (0 past the window)
     const bool whole = (j < n_win) ? j <= jw_hi : (!SYM && BN <= n_keyrows);
     const long long base = (k_rho + (long long)kt * BN * k_rowstride) * 2;
@@ -770,7 +774,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       if (wave == NW - 1) {
         const int slot = min((tr.lo + j) * BN + lane, a.S - 1);
         dma_dword(reinterpret_cast<const char *>(a.slot_pos + (long long)b * a.S),
-                  (uint32_t)slot * 4u, stage + (uint32_t)SP_OFF);
+                  (uint32_t)slot * 4u, lds_addr(smem) + (uint32_t)(si * 256));
       }
     }
   };
@@ -935,12 +939,22 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // are filled and lie in the window of every row), 0 = no slot lies in the
   // window of any row (nor is a sink), so the tile adds nothing and is
   // skipped, 2 = partial (masked).
-  auto ring_class = [&](const char *stg, int j) {
+  auto slot_pos_of = [&](int st) {  // slot positions of the tile in stage st
+    return reinterpret_cast<const int *>(smem + st * 256);
+  };
+  // lanes whose slot (lane % BN) of tile j exists, from the uniform count
+  auto slot_lanes = [&](int j) -> uint64_t {
     const int n_in = min(BN, a.S - (tr.lo + j) * BN);
-    const int sp = reinterpret_cast<const int *>(stg + SP_OFF)[lane % BN];
-    const bool live = (lane % BN) < n_in && sp >= 0 && sp <= pos_hi &&
+    if constexpr (BN == 64) return n_in >= 64 ? ~0ull : (1ull << n_in) - 1;
+    const uint64_t m = n_in >= 32 ? 0xffffffffull : (1ull << n_in) - 1;
+    return m | (m << 32);
+  };
+  auto ring_class = [&](int st, int j) {
+    const int n_in = min(BN, a.S - (tr.lo + j) * BN);
+    const int sp = slot_pos_of(st)[lane % BN];
+    const bool live = sp >= 0 && sp <= pos_hi &&
                       ((long long)sp > (long long)pos_lo - a.W || sp < a.n_sink);
-    if (__builtin_amdgcn_ballot_w64(live) == 0) return 0;
+    if ((__builtin_amdgcn_ballot_w64(live) & slot_lanes(j)) == 0) return 0;
     // every slot in the window of every row (with 32 slots both half-waves
     // hold them all)
     const bool all_in = sp >= 0 && (long long)sp > (long long)pos_hi - a.W && sp <= pos_lo;
@@ -949,20 +963,21 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   };
   // Ring mask: slot k of the tile (k < S) is attended iff its position p has
   // p >= 0 and my_pos - W < p <= my_pos.
-  auto ring_mask = [&](const char *stg, int j, f32x16 *sv) {
-    const int n_in = min(BN, a.S - (tr.lo + j) * BN);
-    const int *spl = reinterpret_cast<const int *>(stg + SP_OFF);
+  auto ring_mask = [&](int st, int j, f32x16 *sv) {
+    // slot c + 4 lh (c the element's constant part) exists iff c < lim
+    const int lim = min(BN, a.S - (tr.lo + j) * BN) - 4 * lh;
+    const int *spl = slot_pos_of(st) + 4 * lh;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int k0 = kb * 32 + 8 * g4 + 4 * lh;
-        const int4 p4 = *reinterpret_cast<const int4 *>(spl + k0);
+        const int c0 = kb * 32 + 8 * g4;
+        const int4 p4 = *reinterpret_cast<const int4 *>(spl + c0);
         const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = pv[i];
-          const bool ok = k0 + i < n_in && p >= 0 && p <= my_pos &&
+          const bool ok = c0 + i < lim && p >= 0 && p <= my_pos &&
                           (p > my_pos - a.W || p < a.n_sink);
           if (!ok) sv[kb][4 * g4 + i] = -INFINITY;
         }
@@ -973,13 +988,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // wave reads the tile.  Their weights are 0 already, but 0 times the NaN or
   // Inf bits an unwritten slot may hold would not be.  Every wave sees the
   // same slot positions, so all take the same branch and the same barrier.
-  auto ring_zero_holes = [&](char *stg, int j) {
-    const int n_in = min(BN, a.S - (tr.lo + j) * BN);
-    const int sp = reinterpret_cast<const int *>(stg + SP_OFF)[lane % BN];
-    const uint64_t hole = __builtin_amdgcn_ballot_w64((lane % BN) >= n_in || sp < 0);
+  auto ring_zero_holes = [&](int st, int j) {
+    const int sp = slot_pos_of(st)[lane % BN];
+    const uint64_t hole = __builtin_amdgcn_ballot_w64(sp < 0) | ~slot_lanes(j);
     if (hole == 0) return;
     constexpr int CPR = D / 8, RPW = 64 / CPR;  // 16-byte chunks per row, rows per store
-    char *vt = stg + Gm::TILE_B;
+    char *vt = smem + SPA + st * STAGE_B + Gm::TILE_B;
 #pragma unroll
     for (int r0 = wave * RPW; r0 < BN; r0 += NW * RPW) {
       const int row = r0 + lane / CPR;
@@ -1046,7 +1060,6 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       }
   };
 
-  const uint32_t a_s0 = lds_addr(smem);
   // ---- main loop: tile j is computed from stage j % NST while the copies of
   // tiles j+1 .. j+NST-1 are in flight.  Step j waits for its own tile and
   // barriers (so every wave is also done with tile j-1), then reuses tile
@@ -1058,13 +1071,13 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     constexpr int st = decltype(stage)::value;
     wait_dma_keep(NST == 2 ? 0 : min(n_tiles - 1 - j, NST - 2) * NCOPY);
     __syncthreads();
-    if (j + NST - 1 < n_tiles) issue(j + NST - 1, a_s0 + (uint32_t)(((st + NST - 1) % NST) * STAGE_B));
+    if (j + NST - 1 < n_tiles) issue(j + NST - 1, (st + NST - 1) % NST);
     // a wave computes the tiles of its rows' band and the tiles of global keys
-    char *ks = smem + st * STAGE_B;
+    char *ks = smem + SPA + st * STAGE_B;
     int rc = 1;  // ring mode: tile class (0 = nothing attended, skip)
     if constexpr (RING) {
-      ring_zero_holes(ks, j);
-      rc = has_rows ? ring_class(ks, j) : 0;
+      ring_zero_holes(st, j);
+      rc = has_rows ? ring_class(st, j) : 0;
     }
     const bool comp = (n_glob > 0 && j >= n_win) ? has_rows : (unsigned)(j - jc_lo) <= jc_span;
     if (rc != 0 && comp) {
@@ -1072,7 +1085,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       U4 pu[PK];
       qk(ks, sv);
       if constexpr (RING) {
-        if (rc == 2) ring_mask(ks, j, sv);
+        if (rc == 2) ring_mask(st, j, sv);
       } else {
         const uint64_t gcols = glob_cols(j);
         if (gcols || !tile_full(j)) mask(j, sv, gcols);
@@ -1084,7 +1097,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   };
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < n_tiles) issue(p, a_s0 + (uint32_t)(p * STAGE_B));
+    if (p < n_tiles) issue(p, p);
   if constexpr (!SYM && !RING) {
     if (a.rope) {
       // Rotary positions, rotate-half pairs (c, c + D/2): this lane holds
