@@ -316,7 +316,7 @@ template <int D, bool GPROJ>
 __device__ inline void gp_load_q(bf16x8 *qf, const FwdArgs &a, int b, int h, int pos) {
   const uint16_t *qsrc = static_cast<const uint16_t *>(GPROJ ? a.qg : a.q);
   const uint16_t *qr = qsrc + (long long)b * a.q_sb + (long long)pos * a.q_st + (long long)h * D;
-  const int q4 = (threadIdx.x & 63) >> 4;
+  const int q4 = (thread_x() & 63) >> 4;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const U4 *>(qr + ks * 32 + q4 * 8));
 }
@@ -324,7 +324,7 @@ __device__ inline void gp_load_q(bf16x8 *qf, const FwdArgs &a, int b, int h, int
 template <int D, bool GPROJ>
 __device__ inline void gp_load(GlobalPart<D> &g, const FwdArgs &a, const GlobalList &gl, int b, int h,
                                int kvh, int rho, int dil, int n_cls, int row0) {
-  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int lane = thread_x() & 63, l16 = lane & 15, q4 = lane >> 4;
   // the first global positions before the K, V loads, so that the query
   // loads wait for this load only
   const int pos0 = l16 < a.G ? gl.idx[b * a.G + l16] : 0;
@@ -364,7 +364,7 @@ __device__ inline void gp_finish(GlobalPart<D> &g, const FwdArgs &a, const Globa
                                  int b, int h, int rho, int dil, int n_cls, int row0) {
   using Gm = Geo<D>;
   constexpr int DB = D / 16, CPR = D / 8;
-  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int lane = thread_x() & 63, l16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
   for (int i = 0; i < GlobalPart<D>::NV; ++i) {
     const int idx = i * 64 + lane, r = idx / CPR, ch = idx % CPR;
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   constexpr int KB = BN / 32;    // 32-key blocks of S^T per tile
   constexpr int PK = BN / 16;    // 16-key k-steps of the PV product per tile
 
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   __builtin_assume(wave >= 0 && wave < NW);
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   int tile_row0, tile_rows;     // workgroup's query rows (for the tile schedule)
   if constexpr (!SYM && !CDIL) {
     const int nblk = a.B * a.n_hg * a.n_qt;
-    const int lid = xcd_remap(blockIdx.x, nblk);
+    const int lid = xcd_remap(group_x(), nblk);
     const int qt = a.n_qt - 1 - (lid % a.n_qt);  // heavy (full-band) tiles first
     const int rest = lid / a.n_qt;
     const int hg = rest % a.n_hg;
@@ -523,11 +523,11 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // share its L2.  Workgroups past their XCD's range exit at once.
     int lid;
     if constexpr (CDIL) {
-      const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+      const int x = group_x() & 7, i = group_x() >> 3;
       lid = a.xcd_off[x] + i;
       if (lid >= a.xcd_off[x + 1]) return;
     } else {
-      lid = xcd_remap(blockIdx.x, nblk);
+      lid = xcd_remap(group_x(), nblk);
     }
     b = lid / a.tiles_per_batch;
     const int rem = lid % a.tiles_per_batch;
@@ -1284,8 +1284,8 @@ __global__ __launch_bounds__(256) void global_combine_kernel(const FwdArgs a, co
   __shared__ float s_m[RPP];
   __shared__ float s_l[RPP];
   __shared__ float4 s_o[RPP][LPR];
-  const int u = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int u = group_x(), h = group_y(), b = group_z();
+  const int tid = thread_x();
   const int c = tid % LPR, j = tid / LPR;
   const int nb = class_tiles(a.T, a.dil[h], kRowsPerWave);
   const float *ws = a.gws + (((long long)b * a.Hq + h) * a.G + u) * a.gnb * PS;

@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void split_kernel(const SplitArgs a, const Glo
   __shared__ float ml[kMaxQ][2];
   __shared__ uint8_t key_ok[kMaxChunk];  // key r of the chunk is attended
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = group_x(), kvh = group_y(), b = group_z();
+  const int tid = thread_x(), lane = tid & 63, wave = tid >> 6;
   const int c0 = split * a.chunk;
   const int c1 = min(a.n_keys, c0 + a.chunk);
   const int n = c1 - c0;
@@ -202,8 +202,8 @@ __device__ inline float block_reduce(float x, bool is_max, float *red) {
     x = is_max ? fmaxf(x, y) : x + y;
   }
   if constexpr (D > 64) {
-    const int wv = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wv] = x;
+    const int wv = thread_x() >> 6;
+    if ((thread_x() & 63) == 0) red[wv] = x;
     __syncthreads();
     x = is_max ? fmaxf(red[0], red[1]) : red[0] + red[1];
     __syncthreads();
@@ -214,8 +214,8 @@ __device__ inline float block_reduce(float x, bool is_max, float *red) {
 template <int D, bool F32, bool DECODE>
 __global__ __launch_bounds__(128) void combine_kernel(const SplitArgs a, const GlobalList gl, int G) {
   __shared__ float red[2];
-  const int qi = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int d = threadIdx.x;
+  const int qi = group_x(), kvh = group_y(), b = group_z();
+  const int d = thread_x();
   const long long base = (((long long)b * a.NKV + kvh) * a.NQ + qi) * a.S;
   const float *ws = a.ws + base * (D + 2);
   float m_loc = -INFINITY;
@@ -365,13 +365,13 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
   // [wave][parity][pair][row group][query]
   __shared__ uint32_t ppair_all[NWG][2][NPAIR][RG][QG];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = thread_x() & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
   const int lq = lane & 31, lh = lane >> 5;
-  const int split = NSW > 0 ? wave : blockIdx.x;
+  const int split = NSW > 0 ? wave : group_x();
   auto &ppair = ppair_all[wave];
-  const int kvh = blockIdx.y / n_pass, q0 = (blockIdx.y % n_pass) * QG;
-  const int b = blockIdx.z;
+  const int kvh = group_y() / n_pass, q0 = (group_y() % n_pass) * QG;
+  const int b = group_z();
   const int nq = min(QG, a.NQ - q0);
   // Keys of this wave: with NSW = 0 the split's chunk [c0, c1) in 32-key
   // blocks; with NSW > 0 the waves interleave 32-key blocks (wave w takes
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
       m_ml[wave][lq][1] = l_run;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < QG * D; i += 64 * NSW) {
+    for (int i = thread_x(); i < QG * D; i += 64 * NSW) {
       const int q = i / D, d = i % D;
       if (q >= nq) continue;
       float M = -INFINITY;
@@ -659,23 +659,23 @@ hipError_t run(const SplitArgs &a, const GlobalList *gl, int G, hipStream_t st) 
 __global__ void cache_write_kernel(const char *kn, const char *vn, const int *pos, char *kc,
                                    char *vc, int *slot_pos, int L, int S, int Hkv, int row_bytes,
                                    int n_sink) {
-  const int hk = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int hk = group_x(), t = group_y(), b = group_z();
   const int p = pos[(long long)b * L + t];
   if (p < 0) return;  // documented precondition; never index with a negative slot
   // sink tokens (p < n_sink) keep slot p; the rest roll over the other slots
   const int slot = (p < n_sink) ? p : n_sink + (p - n_sink) % (S - n_sink);
   const long long src = (((long long)b * L + t) * Hkv + hk) * row_bytes;
   const long long dst = (((long long)b * Hkv + hk) * S + slot) * row_bytes;
-  for (int i = threadIdx.x * 4; i < row_bytes; i += blockDim.x * 4) {
+  for (int i = thread_x() * 4; i < row_bytes; i += group_size_x() * 4) {
     *reinterpret_cast<uint32_t *>(kc + dst + i) = *reinterpret_cast<const uint32_t *>(kn + src + i);
     *reinterpret_cast<uint32_t *>(vc + dst + i) = *reinterpret_cast<const uint32_t *>(vn + src + i);
   }
-  if (hk == 0 && threadIdx.x == 0) slot_pos[(long long)b * S + slot] = p;
+  if (hk == 0 && thread_x() == 0) slot_pos[(long long)b * S + slot] = p;
 }
 
 __global__ void debug_mask_kernel(int mode, int T, int w_or_r, int dil, const GlobalList gl, int G,
                                   uint8_t *mask) {
-  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  const long long i = group_x() * (long long)group_size_x() + thread_x();
   if (i >= (long long)T * T) return;
   const int t = (int)(i / T), s = (int)(i % T);
   // the row's key bounds of the banded kernels (row_key_bounds), in the

@@ -20,6 +20,16 @@
 
 namespace swa {
 
+// Work-item and workgroup ids read straight from the hardware.  The threadIdx,
+// blockIdx and blockDim accessors go through device-library functions that
+// kernels built with -mno-amdgpu-ieee cannot inline, so each use would be a
+// call (whose entry waits for every outstanding memory operation).
+__device__ inline int thread_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ inline int group_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ inline int group_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ inline int group_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+__device__ inline int group_size_x() { return (int)__builtin_amdgcn_workgroup_size_x(); }
+
 // ---------------------------------------------------------------- predicates
 
 // Causal window ([KB] §2 N_t, §3 mask): key s is attended by query t iff t-W < s <= t.
