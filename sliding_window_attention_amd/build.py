@@ -17,7 +17,9 @@ SOURCES = ["swa_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "split_kv.hip", "rope.h
 
 # The bf16 kernels never create NaNs (masked scores are -inf, never NaN), so
 # they are built without IEEE NaN quieting: fmax then needs no canonicalising
-# moves in front of every MFMA result.  Infinities stay honoured.
+# moves in front of every MFMA result.  Infinities stay honoured.  (Such code
+# cannot inline the device-library accessors behind threadIdx / blockIdx, so
+# these sources read the ids through the hardware builtins instead.)
 RELAXED_NAN = {"fwd_bf16.hip", "split_kv.hip"}
 
 FLAGS = [
