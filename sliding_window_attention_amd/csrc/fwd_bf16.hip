@@ -579,12 +579,33 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   const uint16_t *vbase = vg + (long long)b * a.k_sb + (long long)kvh * a.k_sh;
   const int n_keyrows = RING ? a.S : n_cls;  // key rows of this (batch, head)
 
+  // ring mode: this lane's query position, loaded ahead of Q so that waiting
+  // for it does not wait for Q
+  int q_pos_ld = 0;
+  if constexpr (RING)
+    if (row0 + lq < n_cls) q_pos_ld = a.q_pos[(long long)b * a.T + row0 + lq];
+
+  // -------- Q (B operand of S^T = K Q^T): lane holds row lq, columns 16ks + 8lh .. +7
+  bf16x8 qf[KS_QK];
+  {
+    const int r = row0 + lq;
+    const uint16_t *qp = qg + (long long)b * a.q_sb + (long long)h * D +
+                         (long long)rho * a.q_st + (long long)r * q_rowstride;
+#pragma unroll
+    for (int ks = 0; ks < KS_QK; ++ks) {
+      U4 u = U4{{0, 0, 0, 0}};
+      if (r < n_cls) u = *reinterpret_cast<const U4 *>(qp + ks * 16 + lh * 8);
+      qf[ks] = as_bf16x8(u);
+    }
+  }
+
   // -------- global keys of symmetric mode, sink tokens of causal sink mode ->
   // LDS: the K rows, then (GKV_ROWS rows further) the V rows, copied straight
-  // into LDS, RPI rows per wave instruction.  They are issued before every
-  // other load, so the first tile step's wait covers them and its barrier
-  // publishes them to the other waves; they are read after the band.  Rows
-  // past the last one repeat it (inside the GKV_ROWS-row regions).
+  // into LDS, RPI rows per wave instruction.  They are issued after Q (they
+  // wait for the global positions' scalar loads) and before the tile copies,
+  // so the first tile step's wait covers them and its barrier publishes them
+  // to the other waves; they are read after the band.  Rows past the last one
+  // repeat it (inside the GKV_ROWS-row regions).
   char *const gkv = smem + SMEM_B;
   // sink tokens that exist (positions below both n_sink and T)
   const int n_sink = CSINK ? min(a.n_sink, n_cls) : 0;
@@ -607,26 +628,6 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       }
       const uint16_t *src = (isv ? vbase : kbase) + (long long)pos * a.k_st + (lane % CPR) * 8;
       dma_addr(src, lds_addr(gkv) + (uint32_t)((isv * GKV_ROWS + r0i) * Gm::ROWB));
-    }
-  }
-
-  // ring mode: this lane's query position, loaded ahead of Q so that waiting
-  // for it does not wait for Q
-  int q_pos_ld = 0;
-  if constexpr (RING)
-    if (row0 + lq < n_cls) q_pos_ld = a.q_pos[(long long)b * a.T + row0 + lq];
-
-  // -------- Q (B operand of S^T = K Q^T): lane holds row lq, columns 16ks + 8lh .. +7
-  bf16x8 qf[KS_QK];
-  {
-    const int r = row0 + lq;
-    const uint16_t *qp = qg + (long long)b * a.q_sb + (long long)h * D +
-                         (long long)rho * a.q_st + (long long)r * q_rowstride;
-#pragma unroll
-    for (int ks = 0; ks < KS_QK; ++ks) {
-      U4 u = U4{{0, 0, 0, 0}};
-      if (r < n_cls) u = *reinterpret_cast<const U4 *>(qp + ks * 16 + lh * 8);
-      qf[ks] = as_bf16x8(u);
     }
   }
 
