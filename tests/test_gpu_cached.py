@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import pool
 from sliding_window_attention_amd import binding as bd
 from sliding_window_attention_amd import inputs as inp
 from gpu_util import TOL_BF16, TOL_F32, TOL_LSE_BF16, TOL_LSE_F32, banner, dev, host, max_err
@@ -129,15 +130,26 @@ def test_single_token_chunk_equals_decode():
     assert max_err(oc[:, 0], ro) <= TOL_BF16
 
 
-def test_cached_full_size_sampled_rows():
-    # the timed chunked-prefill workload, in the launch configuration bench.py
-    # times; 48 sampled (request, token) rows checked against the oracle
+def test_cached_full_size_all_rows():
+    # the timed chunked-prefill workload in the launch configuration bench.py
+    # times; every (request, token) row and head against the oracle
     c = inp.C6
     q, kc, vc, sp, qp = inp.chunk_inputs(c)
-    rng = np.random.default_rng(55)
-    b_idx = rng.integers(0, c.B, size=48)
-    t_idx = np.concatenate([[0, c.L - 1, 1, c.L - 2], rng.integers(0, c.L, size=44)])
-    _compare(q, kc, vc, sp, qp, c.W, "bf16", rows=(b_idx, t_idx))
+    banner(f"prefill_cached full size B={c.B} L={c.L} S={c.S} W={c.W} all rows")
+    o, lse = bd.prefill_cached(dev(q), dev(kc), dev(vc), dev(sp), dev(qp), c.W, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), host(lse)
+    worst = 0.0
+    for rc, (ro, rl) in pool.run_rows(oracle.swa_prefill_cached,
+                                      (inp.widen(q), inp.widen(kc), inp.widen(vc), sp.numpy(),
+                                       qp.numpy()), np.arange(c.L), dict(W=c.W)):
+        e = max_err(host(o[:, rc]), ro)
+        worst = max(worst, e)
+        assert e <= TOL_BF16, f"tokens {rc[0]}..{rc[-1]} max err {e}"
+        assert np.array_equal(np.isneginf(lse[:, :, rc]), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        assert max_err(lse[:, :, rc][fin], rl[fin]) <= TOL_LSE_BF16, f"lse tokens {rc[0]}..{rc[-1]}"
+    banner(f"prefill_cached: all {c.B * c.L} rows x all heads, max err {worst:.3e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import pool
 from sliding_window_attention_amd import binding as bd
 from sliding_window_attention_amd import inputs as inp
 from gpu_util import TOL_BF16, TOL_F32, TOL_LSE_BF16, TOL_LSE_F32, banner, dev, host, max_err
@@ -82,18 +83,25 @@ def test_all_ones_is_prefill():
     assert torch.equal(a, b)
 
 
-def test_prefill_dilated_fullsize_sampled():
-    # the headline shape with dilations 1, 2 and 4 on groups of heads; sampled rows
+def test_prefill_dilated_fullsize_row_set():
+    # the timed dilated workload (headline shape, dilations 1, 2 and 4 on groups
+    # of heads) in bench.py's launch configuration: rows [0, W+256), [T-256, T)
+    # and 1024 seeded random rows, all heads
     c = inp.C2
     dil = [1] * 16 + [2] * 8 + [4] * 8
     q, k, v = inp.prefill_inputs(c)
-    banner(f"prefill_dilated full size T={c.T} W={c.W}")
+    banner(f"prefill_dilated full size T={c.T} W={c.W} row set")
     o, lse = bd.prefill_dilated(dev(q), dev(k), dev(v), c.W, dil, return_lse=True)
     torch.cuda.synchronize()
+    o, lse = o.cpu(), host(lse)
     rng = np.random.default_rng(77)
-    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(c.T - 40, c.T),
-                                     rng.integers(0, c.T, 40)]))
-    ro, rl = oracle.swa_prefill(inp.widen(q), inp.widen(k), inp.widen(v), c.W, rows=rows,
-                                dilation=dil)
-    assert max_err(host(o)[:, rows], ro) <= TOL_BF16
-    assert max_err(host(lse)[:, :, rows], rl) <= TOL_LSE_BF16
+    rows = np.unique(np.concatenate([np.arange(0, c.W + 256), np.arange(c.T - 256, c.T),
+                                     rng.integers(0, c.T, 1024)]))
+    worst = 0.0
+    for rc, (ro, rl) in pool.run_rows(oracle.swa_prefill, (inp.widen(q), inp.widen(k), inp.widen(v)),
+                                      rows, dict(W=c.W, dilation=dil)):
+        e = max_err(host(o[:, rc]), ro)
+        worst = max(worst, e)
+        assert e <= TOL_BF16, f"rows {rc[0]}..{rc[-1]} max err {e}"
+        assert max_err(lse[:, :, rc], rl) <= TOL_LSE_BF16, f"lse rows {rc[0]}..{rc[-1]}"
+    banner(f"prefill_dilated: {len(rows)} rows x all heads, max err {worst:.3e}")

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import pool
 from sliding_window_attention_amd import binding as bd
 from sliding_window_attention_amd import inputs as inp
 from gpu_util import TOL_BF16, TOL_F32, TOL_LSE_BF16, TOL_LSE_F32, banner, dev, host, max_err
@@ -113,17 +114,27 @@ def test_sink_ring_chunks_equal_prefill(dtype):
     assert max_err(oc, ro) <= tol
 
 
-def test_prefill_sinks_full_size_sampled_rows():
+def test_prefill_sinks_full_size_row_set():
     # the timed sinks workload (headline shape, 4 sink tokens, per-head sink
-    # scores) in bench.py's launch configuration; sampled rows vs the oracle
+    # scores) in bench.py's launch configuration: rows [0, W+256) (the ramp,
+    # where the sinks lie inside the window, and the first rows whose window
+    # has left them), [T-256, T) and 1024 seeded random rows, all heads
     c = inp.C2
     q, k, v = inp.prefill_inputs(c)
     z = _logits(c.Hq, 95)
-    banner("prefill_sinks full size")
-    o = host(bd.prefill_sinks(dev(q), dev(k), dev(v), c.W, n_sink=4,
-                              sink_logit=dev(torch.from_numpy(z))))
+    banner("prefill_sinks full size row set")
+    o, lse = bd.prefill_sinks(dev(q), dev(k), dev(v), c.W, n_sink=4,
+                              sink_logit=dev(torch.from_numpy(z)), return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), host(lse)
     rng = np.random.default_rng(96)
-    rows = sorted(set([0, 3, 4, c.W - 1, c.W, c.W + 1, c.T - 1] + rng.integers(0, c.T, 25).tolist()))
-    ro, _ = oracle.swa_prefill(inp.widen(q), inp.widen(k), inp.widen(v), c.W, rows=rows, n_sink=4,
-                               sink_logit=z.astype(np.float64))
-    assert max_err(o[:, rows], ro) <= TOL_BF16
+    rows = np.unique(np.concatenate([np.arange(0, c.W + 256), np.arange(c.T - 256, c.T),
+                                     rng.integers(0, c.T, 1024)]))
+    worst = 0.0
+    for rc, (ro, rl) in pool.run_rows(oracle.swa_prefill, (inp.widen(q), inp.widen(k), inp.widen(v)),
+                                      rows, dict(W=c.W, n_sink=4, sink_logit=z.astype(np.float64))):
+        e = max_err(host(o[:, rc]), ro)
+        worst = max(worst, e)
+        assert e <= TOL_BF16, f"rows {rc[0]}..{rc[-1]} max err {e}"
+        assert max_err(lse[:, :, rc], rl) <= TOL_LSE_BF16, f"lse rows {rc[0]}..{rc[-1]}"
+    banner(f"prefill_sinks: {len(rows)} rows x all heads, max err {worst:.3e}")
