@@ -685,6 +685,24 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     fb.lo = uni(fb.lo);
     fb.hi = uni(fb.hi);
   }
+  // 64-key tiles: the first window tile of a wave may start, and its last
+  // window tile end, with a whole 32-key block that no row of the wave attends
+  // (its band starts or ends mid-tile).  That block is neither multiplied nor
+  // exponentiated: tile jh0 computes only its block 1, tile jh1 only block 0.
+  // (A tile cannot be both jh0 and jh1: both its blocks would then lie outside
+  // the band, and the tile would not be in the wave's range.)
+  int jh0 = 1 << 30, jh1 = 1 << 30;
+  if constexpr (!RING && KB > 1) {
+    if (has_rows) {
+      // the 32-key blocks some row of the wave attends: [ab.lo, ab.hi]
+      const TileRange ab = SYM ? sym_tile_range(row0, w_last, a.W, n_cls, 32)
+                               : causal_tile_range(row0, w_last, a.W, 32);
+      if (ab.lo & 1) jh0 = wr.lo - tr.lo;     // block 2 wr.lo < ab.lo
+      if (!(ab.hi & 1)) jh1 = wr.hi - tr.lo;  // block 2 wr.hi + 1 > ab.hi
+    }
+    jh0 = uni(jh0);
+    jh1 = uni(jh1);
+  }
   jc_lo = uni(jc_lo);
   jf_lo = uni(jf_lo);
   jc_span = (unsigned)uni((int)jc_span);
@@ -819,29 +837,32 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   float m_use = 0.f, m_thr = -INFINITY;
   const int my_row = row0 + lq;
 
-  // ---- building blocks.  Accumulator element (kb, e) of S^T holds key
-  // 32kb + 8(e/4) + 4lh + (e%4) of the tile, for query row my_row.
-  auto qk = [&](const char *ks, f32x16 *sv) {
+  // ---- building blocks.  They work on NB consecutive 32-key blocks of the
+  // staged tile starting at block B0 (B0 = 0, NB = KB: the whole tile), both
+  // compile-time constants.  Accumulator element (kb, e) of S^T holds key
+  // 32(B0 + kb) + 8(e/4) + 4lh + (e%4) of the tile, for query row my_row.
+  auto qk = [&](const char *ks, f32x16 *sv, auto b0, auto nb) {
+    constexpr int B0 = decltype(b0)::value, NB = decltype(nb)::value;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sv[kb] = f32x16{};
+    for (int kb = 0; kb < NB; ++kb) sv[kb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KS_QK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const U4 u = *reinterpret_cast<const U4 *>(ks + kb * 32 * Gm::ROWB + kop[kk]);
+      for (int kb = 0; kb < NB; ++kb) {
+        const U4 u = *reinterpret_cast<const U4 *>(ks + (B0 + kb) * 32 * Gm::ROWB + kop[kk]);
         sv[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(u), qf[kk], sv[kb], 0, 0, 0);
       }
   };
-  // row max over the tile, in log2 units (sl2 = scale * log2 e)
-  // this lane's share of its row max over the tile (its half of the keys), in
-  // raw score units: three-input max chains
-  auto rowmax = [&](const f32x16 *sv) {
+  // this lane's share of its row max over the blocks (its half of the keys),
+  // in raw score units: three-input max chains
+  auto rowmax = [&](const f32x16 *sv, auto nb) {
+    constexpr int NB = decltype(nb)::value;
     float mx = fmaxf(fmaxf(sv[0][0], sv[0][1]), sv[0][2]);
 #pragma unroll
     for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, sv[0][e]), sv[0][e + 1]);
     mx = fmaxf(mx, sv[0][15]);
 #pragma unroll
-    for (int kb = 1; kb < KB; ++kb)
+    for (int kb = 1; kb < NB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, sv[kb][e]), sv[kb][e + 1]);
     return mx;
@@ -865,13 +886,16 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       m_thr = (m_run == -INFINITY) ? -INFINITY : (m_run + kLazy) / a.sl2;
     }
   };
-  auto exp_pack = [&](f32x16 *sv, U4 *pu) {
+  // P = 2^(s sl2 - m) over the blocks, packed to bf16 as the B operand of the
+  // P.V product: 2 NB key steps of 16
+  auto exp_pack = [&](f32x16 *sv, U4 *pu, auto nb) {
+    constexpr int NB = decltype(nb)::value;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sv[kb][e] = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], a.sl2, -m_use));
 #pragma unroll
-    for (int kk = 0; kk < PK; ++kk) {
+    for (int kk = 0; kk < 2 * NB; ++kk) {
       const int kb = kk >> 1, e0 = (kk & 1) * 8;
 #pragma unroll
       for (int w = 0; w < 4; ++w) pu[kk].w[w] = pack_bf16(sv[kb][e0 + 2 * w], sv[kb][e0 + 2 * w + 1]);
@@ -881,19 +905,20 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // share is added once, before the epilogue.
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-    for (int kk = 0; kk < PK; ++kk)
+    for (int kk = 0; kk < 2 * NB; ++kk)
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pu[kk].w[w]), ones, l_run, false);
   };
-  // O^T += V^T P^T : key steps of 16
-  auto pv = [&](const char *vs, const U4 *pu) {
+  // O^T += V^T P^T : key steps of 16 over the blocks
+  auto pv = [&](const char *vs, const U4 *pu, auto b0, auto nb) {
+    constexpr int B0 = decltype(b0)::value, NB = decltype(nb)::value;
 #pragma unroll
-    for (int kk = 0; kk < PK; ++kk) {
+    for (int kk = 0; kk < 2 * NB; ++kk) {
       const bf16x8 pb = as_bf16x8(pu[kk]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char *p0 = vs + kk * 16 * Gm::ROWB + vop[db];
+        const char *p0 = vs + (2 * B0 + kk) * 16 * Gm::ROWB + vop[db];
         const bf16x8 vt = tr_read8(p0, p0 + 8 * Gm::ROWB);
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pb, acc_o[db], 0, 0, 0);
       }
@@ -1008,9 +1033,11 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   // the class length.
   int lo_key, hi_key;
   row_key_bounds(SYM, my_row, a.W, n_cls, &lo_key, &hi_key);
-  // mask of a partial tile: the window predicate (global positions left out
-  // when gcols marks some), or for a tile of global keys the existing globals
-  auto mask = [&](int j, f32x16 *sv, uint64_t gcols) {
+  // mask of a partial tile over the blocks B0 .. B0+NB-1: the window
+  // predicate (global positions left out when gcols marks some), or for a
+  // tile of global keys the existing globals
+  auto mask = [&](int j, f32x16 *sv, uint64_t gcols, auto b0, auto nb) {
+    constexpr int B0 = decltype(b0)::value, NB = decltype(nb)::value;
     if (j < n_win) {
       // key of element (kb, e) = tile base + 4*lh + c(kb, e); compare c with
       // this lane's bounds shifted to the same origin
@@ -1020,10 +1047,10 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
         // global positions of this class in the tile: counted in the global tile
         const uint64_t gl_lane = gcols >> (4 * lh);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+            const int c = (B0 + kb) * 32 + 8 * (e >> 2) + (e & 3);
             if (c < lo || c > hi || ((gl_lane >> c) & 1)) sv[kb][e] = -INFINITY;
           }
         return;
@@ -1033,15 +1060,15 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       const int lo2 = hi >= lo ? lo : (1 << 30);
       const uint32_t span = hi >= lo ? (uint32_t)(hi - lo) : 0u;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < NB; ++kb) {
         if constexpr (KB > 1) {
           // a 32-key block inside every row's window needs no mask
-          const int blk = (tr.lo + j) * (BN / 32) + kb;
+          const int blk = (tr.lo + j) * (BN / 32) + B0 + kb;
           if ((unsigned)(blk - fb.lo) <= (unsigned)(fb.hi - fb.lo)) continue;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+          const int c = (B0 + kb) * 32 + 8 * (e >> 2) + (e & 3);
           if ((uint32_t)(c - lo2) > span) sv[kb][e] = -INFINITY;
         }
       }
@@ -1053,10 +1080,10 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     // (glob_cols), so each key is counted once.
     const int hi = min(a.G - (j - n_win) * BN, BN) - 1 - 4 * lh;  // this lane's origin
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int c = kb * 32 + 8 * (e >> 2) + (e & 3);
+        const int c = (B0 + kb) * 32 + 8 * (e >> 2) + (e & 3);
         if (c > hi) sv[kb][e] = -INFINITY;
       }
   };
@@ -1081,19 +1108,31 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
       rc = has_rows ? ring_class(st, j) : 0;
     }
     const bool comp = (n_glob > 0 && j >= n_win) ? has_rows : (unsigned)(j - jc_lo) <= jc_span;
-    if (rc != 0 && comp) {
-      f32x16 sv[KB];
-      U4 pu[PK];
-      qk(ks, sv);
+    // the computed blocks B0 .. B0+NB-1 of the tile
+    auto blocks = [&](auto b0, auto nb) {
+      constexpr int NB = decltype(nb)::value;
+      f32x16 sv[NB];
+      U4 pu[2 * NB];
+      qk(ks, sv, b0, nb);
       if constexpr (RING) {
         if (rc == 2) ring_mask(st, j, sv);
       } else {
         const uint64_t gcols = glob_cols(j);
-        if (gcols || !tile_full(j)) mask(j, sv, gcols);
+        if (gcols || !tile_full(j)) mask(j, sv, gcols, b0, nb);
       }
-      rescale(rowmax(sv));
-      exp_pack(sv, pu);
-      pv(ks + Gm::TILE_B, pu);
+      rescale(rowmax(sv, nb));
+      exp_pack(sv, pu, nb);
+      pv(ks + Gm::TILE_B, pu, b0, nb);
+    };
+    if (rc != 0 && comp) {
+      if constexpr (!RING && KB > 1) {
+        // the two 32-key halves in turn, each with its own max test; a half
+        // that no row of the wave attends is skipped
+        if (j != jh0) blocks(IntC<0>{}, IntC<1>{});
+        if (j != jh1) blocks(IntC<1>{}, IntC<1>{});
+      } else {
+        blocks(IntC<0>{}, IntC<KB>{});
+      }
     }
   };
 #pragma unroll
