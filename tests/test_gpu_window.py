@@ -315,3 +315,60 @@ def test_decode_zero_query_exact_counts():
     for h in range(c.Hq):
         assert max_err(o_h[:, h], want[:, h // group]) <= TOL_BF16, f"head {h}"
     assert max_err(host(lse), np.broadcast_to(np.log(n)[:, None], (c.B, c.Hq))) <= TOL_LSE_EXACT
+
+
+# ------------------------------------------- 64-key tiles: windows around block edges
+#
+# At d_h = 64 a key tile holds two 32-key blocks, computed in turn, and a block
+# outside every row of a wave is skipped.  Windows whose ends fall just before,
+# on and just after 32- and 64-key boundaries move that skip between the first
+# and the last tile of a wave; q = 0 reads every row's window size out exactly.
+
+@pytest.mark.parametrize("W", [1, 31, 32, 33, 63, 64, 65, 96, 97, 128, 129, 200, 256, 257])
+def test_causal_d64_zero_query_exact_counts(W):
+    # two query heads per key/value head: waves at rows R and R + 32
+    B, T, Hq, Hkv, D = 2, 700, 4, 2, 64
+    q, k, v = _zero_q((B, T, Hq, D), (B, T, Hkv, D), 500 + W)
+    banner(f"causal d64 q = 0 W={W}")
+    o, lse = bd.prefill(dev(q), dev(k), dev(v), W, return_lse=True)
+    torch.cuda.synchronize()
+    vn = inp.widen(v).astype(np.float64)
+    t = np.arange(T)
+    lo = np.maximum(0, t - W + 1)
+    n = (t - lo + 1).astype(np.float64)
+    cs = _prefix(vn, axis=1)                                 # [B, T+1, Hkv, D]
+    want = (cs[:, t + 1] - cs[:, lo]) / n[None, :, None, None]
+    group = Hq // Hkv
+    o_h, lse_h = host(o), host(lse)
+    for h in range(Hq):
+        assert max_err(o_h[:, :, h], want[:, :, h // group]) <= TOL_BF16, f"head {h}"
+        assert max_err(lse_h[:, h], np.broadcast_to(np.log(n), (B, T))) <= TOL_LSE_EXACT, \
+            f"lse head {h}"
+
+
+@pytest.mark.parametrize("r", [1, 31, 32, 33, 63, 64, 65, 100, 128])
+def test_symmetric_d64_zero_query_exact_counts(r):
+    # dilations 1, 2, 3 (class lengths 600, 300, 200): bands starting and
+    # ending mid-tile in every class
+    B, T, H, D = 1, 600, 3, 64
+    dil = [1, 2, 3]
+    q, k, v = _zero_q((B, T, H, D), (B, T, H, D), 700 + r)
+    banner(f"symmetric d64 q = 0 r={r}")
+    o, lse = bd.longformer(dev(q), dev(k), dev(v), r, dil, return_lse=True)
+    torch.cuda.synchronize()
+    vn = inp.widen(v).astype(np.float64)
+    o_h, lse_h = host(o), host(lse)
+    for h in range(H):
+        d = dil[h]
+        want = np.empty((B, T, D))
+        n = np.empty(T)
+        for rho in range(d):
+            pos = np.arange(rho, T, d)
+            ci = np.arange(len(pos))
+            lo = np.maximum(0, ci - r)
+            hi = np.minimum(len(pos) - 1, ci + r)
+            cs = _prefix(vn[:, pos, h], axis=1)
+            want[:, pos] = (cs[:, hi + 1] - cs[:, lo]) / (hi - lo + 1)[None, :, None]
+            n[pos] = hi - lo + 1
+        assert max_err(o_h[:, :, h], want) <= TOL_BF16, f"head {h}"
+        assert max_err(lse_h[:, h], np.log(n)[None]) <= TOL_LSE_EXACT, f"lse head {h}"
