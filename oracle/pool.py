@@ -29,9 +29,10 @@ import numpy as np
 _ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def host_cores(cap=12):
+def host_cores(cap=16):
     """Cores this process may run on, at most ``cap`` (a run on the GPU machine
-    gets a share of 16 CPUs; some are left to the parent)."""
+    gets a share of 16 CPUs, whatever the affinity mask shows; the parent
+    only waits while the workers run)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
