@@ -489,7 +489,6 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
   constexpr int DB = D / 32;     // 32-wide d blocks of O^T
   constexpr int BN = Gm::BN;     // keys per tile
   constexpr int KB = BN / 32;    // 32-key blocks of S^T per tile
-  constexpr int PK = BN / 16;    // 16-key k-steps of the PV product per tile
 
   const int tid = thread_x();
   const int lane = tid & 63;
