@@ -1,17 +1,7 @@
 import os
 import sys
 
-import pytest
-
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
-
-
-def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
-
-
-def pytest_collection_modifyitems(config, items):
-    # Keep GPU tests in one process; nothing to reorder otherwise.
-    return None
+# the "gpu" marker is declared in pytest.ini
