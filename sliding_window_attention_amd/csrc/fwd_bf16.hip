@@ -1301,7 +1301,10 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && MODE == kSymmetric) ? 16 / NW
     if (r < n_cls) {
       const U4 u = *reinterpret_cast<const U4 *>(ost + ost_off(rr, c * 8));
       const long long t_abs = rho + (long long)dil * r;
-      *reinterpret_cast<U4 *>(og + (long long)b * a.q_sb + t_abs * a.q_st + (long long)h * D + c * 8) = u;
+      // written once, never read here: a non-temporal store, so the output
+      // rows do not push the key/value band out of L2
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, u),
+                                  reinterpret_cast<u32x4 *>(og + (long long)b * a.q_sb + t_abs * a.q_st + (long long)h * D + c * 8));
     }
   }
 
