@@ -318,20 +318,53 @@ struct DecBlock {
   int valid;                           // this lane's key (lane & 31) is attended
 };
 
+// The block's key rows, read as whole rows: load i brings rows RG*i .. RG*i +
+// RG-1 (TPR lanes per row, 16 bytes each), so every cache line is used up by
+// the load that fetches it and the loads can be non-temporal.  kst_to_operand
+// then moves them into the MFMA operand layout through the wave's LDS slice.
 template <int D>
 __device__ inline void dec_load_k(DecBlock<D> &blk, const uint16_t *kbase, const SplitArgs &a,
                                   int s0, int c1, int lane) {
   using Bk = DecBlock<D>;
-  const int lq = lane & 31, lh = lane >> 5;
-  const int sk = s0 + lq;
-  if (sk < c1) {
-    const uint16_t *kr = kbase + (long long)sk * a.k_sr + lh * 8;
+  static_assert(Bk::RPL == Bk::KS, "one row-group load per MFMA k-step register");
+  const int g = lane / Bk::TPR, c = lane % Bk::TPR;
 #pragma unroll
-    for (int ks = 0; ks < Bk::KS; ++ks) blk.k[ks] = *reinterpret_cast<const U4 *>(kr + ks * 16);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < Bk::KS; ++ks) blk.k[ks] = U4{{0, 0, 0, 0}};
+  for (int i = 0; i < Bk::RPL; ++i) {
+    const int sk = s0 + Bk::RG * i + g;
+    if (sk < c1) blk.k[i] = load_stream(kbase + (long long)sk * a.k_sr + c * 8);
+    else blk.k[i] = U4{{0, 0, 0, 0}};
   }
+}
+
+// 16-byte chunk c of key row r sits at chunk c ^ kst_swz(r) of the row in LDS:
+// the operand reads (16 lanes at a time, 16 consecutive rows, one logical
+// chunk) then hit 16 distinct bank groups.
+template <int D>
+__device__ inline int kst_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+
+// Key rows from the whole-row layout of dec_load_k to the A-operand layout of
+// S^T = K Q^T (lane: key lane & 31, columns 16 ks + 8 (lane >> 5) .. +7), in
+// place, through this wave's LDS slice kl (32 rows).  One wave writes and reads
+// its own slice; LDS operations of a wave complete in order.  The swizzle of
+// row RG i + g is kst_swz(RG i) ^ kst_swz(g) and that of chunk 2 ks + lh is
+// (2 ks) ^ lh (disjoint bits), so every offset is one per-lane base XOR a
+// constant: two base registers instead of one offset register per load.
+template <int D>
+__device__ inline void kst_to_operand(DecBlock<D> &blk, char *kl, int lane) {
+  using Bk = DecBlock<D>;
+  constexpr int ROWB = 2 * D;
+  const int g = lane / Bk::TPR, c = lane % Bk::TPR;
+  const int lq = lane & 31, lh = lane >> 5;
+  int wbase = g * ROWB + ((c ^ kst_swz<D>(g)) * 16);
+  int rbase = lq * ROWB + ((lh ^ kst_swz<D>(lq)) * 16);
+  // recomputed where used (kept out of loop-invariant registers)
+  asm volatile("" : "+v"(wbase), "+v"(rbase));
+#pragma unroll
+  for (int i = 0; i < Bk::RPL; ++i)
+    *reinterpret_cast<U4 *>(kl + ((wbase ^ (kst_swz<D>(Bk::RG * i) * 16)) + i * Bk::RG * ROWB)) = blk.k[i];
+#pragma unroll
+  for (int ks = 0; ks < Bk::KS; ++ks)
+    blk.k[ks] = *reinterpret_cast<const U4 *>(kl + (rbase ^ (32 * ks)));
 }
 
 template <int D, bool DECODE>
@@ -373,6 +406,8 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
   constexpr int NWG = NSW > 0 ? NSW : 1;  // waves per workgroup
   // [wave][parity][pair][row group][query]
   __shared__ uint32_t ppair_all[NWG][2][NPAIR][RG][QG];
+  // each wave's key block on its way to the MFMA operand layout
+  __shared__ __attribute__((aligned(16))) char kst_all[NWG][32 * 2 * D];
 
   const int lane = thread_x() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
@@ -431,6 +466,7 @@ __global__ __launch_bounds__(64 * (NSW > 0 ? NSW : 1), QG >= 8 ? 1 : 2) void spl
     const int parity = ib & 1;
     const int s_next = c0 + (NSW > 0 ? bstep : 32) * (ib + 1);
     const bool more = ib + 1 < nblk;
+    kst_to_operand<D>(blk, kst_all[wave], lane);
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
