@@ -107,7 +107,9 @@ class ChunkCase:
     seed: int = 0
 
 
-# The workloads (shapes of the pages' examples; see the design doc for the recipe).
+# The workloads: seeded N(0, 1) tensors with the shapes of the pages' examples
+# (n = 16 symmetric table, Mistral-shaped prefill and ring decode, Gemma 3 local
+# layers, Longformer-base).
 C1 = LongformerCase(B=1, T=16, H=1, D=64, r=2, dilation=[1], globals_=[], dtype="f32", seed=1000)
 C2 = PrefillCase(B=1, T=16384, Hq=32, Hkv=8, D=128, W=4096, seed=1001)
 C3 = PrefillCase(B=2, T=32768, Hq=32, Hkv=16, D=128, W=1024, rope=True, seed=1002)
